@@ -1,0 +1,200 @@
+"""Benchmark: fused SDPA forward TFLOP/s on MI355X, h=8, d_k=64, causal and
+non-causal.
+
+One step = one pass of the attention hot path over the long-sequence batch
+[B=4, h=8, n_q=n_k=4096, d=64] bf16 in both modes: mha_sdpa without a mask,
+then mha_sdpa with the causal mask (Q/K/V already resident in HBM).  The
+metric counts algorithmic flops only: 4·d per visible (query, key) pair, so
+the causal half that is skipped is not counted.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line.  Only one GPU is used: there is no multi-GPU path.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = dict(B=4, h=8, n=4096, d=64)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sdpa_fwd_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "transformer_head_scaled_amd", "csrc", "sdpa_fwd.hip")
+
+
+def sdpa_flops(B, h, n_q, n_k, d, causal):
+    pairs = n_q * (n_q + 1) // 2 if causal else n_q * n_k
+    return 4.0 * d * pairs * B * h
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return t.get("noncausal_bytes_per_launch")
+
+
+def cpu_baseline(ins, budget_s=12.0):
+    """The fp64 oracle, untuned, on a bounded sample of the same workload:
+    whole (batch, head) pairs, alternating unmasked and causal, until the
+    time budget is used.  Returns the bench's cpu_baseline object."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        cores = 1
+    Q, K, V = (ins[n][1].astype(np.float64) for n in "QKV")
+    B, h, n, d = Q.shape
+    done, flops, t_total = [], 0.0, 0.0
+    k = 0
+    while t_total < budget_s and k < 2 * B * h:
+        b, i = (k // 2) // h % B, (k // 2) % h
+        causal = k % 2 == 1
+        t0 = time.perf_counter()
+        oracle.attention_head(Q[b, i], K[b, i], V[b, i], 0.125,
+                              oracle.MASK_CAUSAL if causal else oracle.MASK_NONE)
+        t_total += time.perf_counter() - t0
+        flops += sdpa_flops(1, 1, n, n, d, causal)
+        done.append(f"({b},{i},{'causal' if causal else 'none'})")
+        k += 1
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(done)} whole heads of [4,8,4096,64] (alternating unmasked/causal, "
+                      f"first {done[0]} .. last {done[-1]}), {t_total:.1f} s fp64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: libmha runs on one GPU only (no multi-GPU path is built); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from transformer_head_scaled_amd import libmha, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOAD
+    B, h, n, d = w["B"], w["h"], w["n"], w["d"]
+    ins = synth.sdpa_inputs(5, B, h, n, n, d, dtype="bf16")
+
+    def dev_t(st):
+        return torch.from_numpy(st.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    Q, K, V = (dev_t(ins[k][0]) for k in "QKV")
+    O_nc = torch.empty_like(Q)
+    O_c = torch.empty_like(Q)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        libmha.sdpa(Q, K, V, scale=0.125, mask="none", out=O_nc, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        libmha.sdpa(Q, K, V, scale=0.125, mask="causal", out=O_c, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronised on both sides
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-launch kernel durations: HIP events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    nc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    c_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    f_nc = sdpa_flops(B, h, n, n, d, False)
+    f_c = sdpa_flops(B, h, n, n, d, True)
+    ms_per_step = wall * 1e3 / args.steps
+    value = (f_nc + f_c) / (ms_per_step * 1e-3) / 1e12
+
+    # spot parity of what was timed (one head per mode) against the oracle
+    import oracle
+    errs = {}
+    for name, out, mk in (("none", O_nc, oracle.MASK_NONE), ("causal", O_c, oracle.MASK_CAUSAL)):
+        b, i = 1, 5
+        got = out[b, i].float().cpu().numpy()
+        exp, _ = oracle.attention_head(ins["Q"][1][b, i], ins["K"][1][b, i], ins["V"][1][b, i],
+                                       0.125, mk)
+        errs[name] = float(np.abs(got - exp).max())
+
+    ach_nc = f_nc / (nc_ms * 1e-3) / 1e12
+    ach_c = f_c / (c_ms * 1e-3) / 1e12
+    res = {
+        "metric": "SDPA fwd TFLOP/s + % bf16 MFMA peak (h=8,d_k=64; causal & non-causal)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "sdpa_fwd_bf16_b4_h8_n4096_d64_causal+noncausal", "B": B, "h": h,
+                   "n_q": n, "n_k": n, "d_k": d, "d_v": d, "global_batch": B, "seq_len": n,
+                   "parallelism": "none (1 GPU)"},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "modes": {
+            "noncausal": {"tflops": round(ach_nc, 2), "pct_peak": round(100 * ach_nc / PEAK_BF16_TFLOPS, 2),
+                          "kernel_ms": round(nc_ms, 5), "flops": f_nc, "max_abs_err_sampled": errs["none"]},
+            "causal": {"tflops": round(ach_c, 2), "pct_peak": round(100 * ach_c / PEAK_BF16_TFLOPS, 2),
+                       "kernel_ms": round(c_ms, 5), "flops": f_c, "max_abs_err_sampled": errs["causal"]},
+        },
+        "roofline": {"bound": "mfma", "achieved": round(ach_nc, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach_nc / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(),
+                     "kernel": "sdpa_fwd_kernel<bf16, non-causal>"},
+        "roofline_causal": {"bound": "mfma", "achieved": round(ach_c, 2), "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(ach_c / PEAK_BF16_TFLOPS, 4),
+                            "kernel": "sdpa_fwd_kernel<bf16, causal>"},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(ins, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

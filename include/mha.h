@@ -1,0 +1,136 @@
+/*
+ * libmha -- the multi-head attention sublayer of the Transformer on AMD
+ * Instinct MI355X (gfx950).  C ABI.
+ *
+ * Page references (title, section):
+ *   [N] nickwang.xyz, "Lire « Attention Is All You Need » : l'article
+ *       original du Transformer"
+ *   [A] agi-iri.ru, "Attention Is All You Need (на русском)"
+ *   [M] ml-canon.vercel.app, "32 Transformer"
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers named Q, K, V, O, x_*, W*, out, seq_lens, kv_lens and
+ *   workspace are DEVICE pointers (memory of the current HIP device).  The
+ *   caller owns every buffer; the library keeps no pointer after a call
+ *   returns.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream).  A status of MHA_OK means the work was validated and enqueued;
+ *   faults inside a kernel surface at the caller's next synchronisation.
+ * - Every argument is validated on the host before anything is enqueued, so
+ *   an error return never leaves partial output.  Device-side key lengths
+ *   cannot be read without a synchronisation; the kernels clamp each one to
+ *   [0, n_k].
+ * - Tensor pointers must be 16-byte aligned and key-length arrays 4-byte
+ *   aligned (MHA_ERR_INVALID_ARG otherwise).
+ * - All tensors of a call share one dtype; the output has the input dtype.
+ *   Products accumulate in fp32; each output element is rounded once
+ *   (round to nearest even).
+ * - B = 0, h = 0 or n_q = 0 is a successful no-op.  n_k = 0 or a key length
+ *   of 0 gives all-zero output rows (a row with nothing visible).
+ * - The library holds no mutable global state; concurrent calls on
+ *   different streams are safe as long as their buffers do not overlap.
+ * - Setting the environment variable MHA_TRACE=1 logs every dispatch
+ *   (kernel, grid, algorithmic bytes and flops) to stderr.
+ */
+#ifndef LIBMHA_MHA_H
+#define LIBMHA_MHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  BF16 and F16 are 2-byte storage; F32 is 4-byte. */
+typedef enum { MHA_F32 = 0, MHA_BF16 = 1, MHA_F16 = 2 } mha_dtype;
+
+/* MHA_MASK_CAUSAL: query r sees keys c <= r, the position itself included
+ * ([A] §3.2.1; [N] "Trois usages de l'attention dans le modèle", decoder
+ * self-attention).  Only defined for n_q == n_k. */
+typedef enum { MHA_MASK_NONE = 0, MHA_MASK_CAUSAL = 1 } mha_mask_kind;
+
+/* Status codes. */
+enum {
+  MHA_OK = 0,
+  MHA_ERR_INVALID_ARG = -1, /* null pointer, non-finite scale, bad enum   */
+  MHA_ERR_SHAPE = -2,       /* negative/oversized dims, causal n_q != n_k,
+                               self-attention n_q != n_k, d_model % h != 0 */
+  MHA_ERR_DTYPE = -3,       /* dtype value outside mha_dtype               */
+  MHA_ERR_UNSUPPORTED = -4, /* valid but not implemented: head dim, or F32
+                               in mha_forward                               */
+  MHA_ERR_WORKSPACE = -5,   /* workspace given but smaller than required   */
+  MHA_ERR_ALIAS = -6,       /* output overlaps an input or the workspace   */
+  MHA_ERR_HIP = -7          /* a HIP runtime call failed (no device, launch
+                               failure, allocation failure)                 */
+};
+
+/*
+ * Scaled dot-product attention, [N] §3.2.1 eq. (1):
+ *   O = softmax(scale · Q·Kᵀ + mask) · V, one independent softmax per query
+ *   row, masked scores set to -inf before the softmax (weight exactly 0).
+ *
+ * Layouts (row-major, contiguous):
+ *   Q [B, h, n_q, d_k]   K [B, h, n_k, d_k]   V [B, h, n_k, d_v]
+ *   O [B, h, n_q, d_v]  (written)
+ * seq_lens: NULL, or device int32[B]: batch b uses only its first
+ *   seq_lens[b] keys (key padding; clamped to [0, n_k]).  Masked K/V rows
+ *   are never read, so their contents (NaN included) have no effect.
+ * scale: any finite float; the pages use 1/sqrt(d_k).
+ * Supported: BF16/F16 with d_k = d_v = 64 (MFMA flash kernel); F32 with
+ *   d_k = d_v in {16, 32, 64, 128}.
+ * O must not overlap Q, K, V or seq_lens (MHA_ERR_ALIAS).
+ */
+int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype, int64_t B,
+             int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, float scale,
+             int32_t mask_kind, const int32_t* seq_lens, void* stream);
+
+/*
+ * Multi-head attention sublayer, [N] §3.2.2 ("Attention multi-têtes"):
+ *   out = Concat(head_1, ..., head_h) · Wo,
+ *   head_i = Attention(x_q·Wq_i, x_kv·Wk_i, x_kv·Wv_i) with scale 1/sqrt(d_k).
+ * No bias, no dropout, no residual/normalisation (outside the sublayer).
+ *
+ * Layouts (row-major, contiguous):
+ *   x_q  [B, n_q, d_model]            queries' source (decoder side)
+ *   x_kv [B, n_k, d_model] or NULL    keys'/values' source; NULL or == x_q
+ *                                     means self-attention (n_k must equal n_q);
+ *                                     the encoder output for cross-attention
+ *   Wq, Wk, Wv [d_model, h·d_k]       multiplied on the right (x·W); head i
+ *                                     owns columns [i·d_k, (i+1)·d_k)
+ *   Wo [h·d_k, d_model]               row blocks in the same head order
+ *   out [B, n_q, d_model]             (written)
+ * d_k = d_v = d_model / h.  Supported: BF16/F16 with d_k = 64.
+ * mask_kind: NONE (encoder self / cross) or CAUSAL (decoder self).
+ * kv_lens: NULL or device int32[B], key padding as in mha_sdpa.
+ * workspace: device memory of at least mha_forward_workspace_size() bytes,
+ *   256-byte aligned, used for the projected Q/K/V and the concat of heads;
+ *   its contents are undefined afterwards.  NULL: the library allocates and
+ *   frees stream-ordered (hipMallocAsync / hipFreeAsync) inside the call.
+ * out must not overlap any input or the workspace (MHA_ERR_ALIAS).
+ */
+int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* Wk,
+                const void* Wv, const void* Wo, void* out, int32_t dtype, int64_t B,
+                int64_t n_q, int64_t n_k, int64_t d_model, int32_t h, int32_t mask_kind,
+                const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mha_forward needs for these sizes (0 for invalid sizes). */
+size_t mha_forward_workspace_size(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model,
+                                  int32_t h, int32_t dtype);
+
+/* Static description of a status code (never NULL). */
+const char* mha_status_string(int status);
+
+/* Thread-local detail of the last error returned on this thread ("" if
+ * none).  Valid until the next libmha call on the same thread. */
+const char* mha_last_error(void);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int mha_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMHA_MHA_H */

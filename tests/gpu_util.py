@@ -1,0 +1,75 @@
+"""Helpers for the GPU tests: host arrays <-> device tensors, and adapters
+that run the pins of ``tests/pins.py`` through libmha.
+
+Inputs always come from numpy (seeded); they are rounded to the device dtype
+on the host (``synth.round_to``), the rounded values go to both sides, and
+results come back as float64 for comparison with the fp64 oracle.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from transformer_head_scaled_amd import libmha, synth  # noqa: E402
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2}
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    libmha.lib()   # raises (fails the test) if the library is not built
+
+
+def note(msg):
+    """Print and flush what names the case before a GPU step."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(storage, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(storage).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(storage)).cuda()
+
+
+def from_dev(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rounded(x, dtype):
+    """Round a float array to the device dtype: (storage, float64 values)."""
+    st, v = synth.round_to(np.asarray(x, dtype=np.float32), dtype)
+    return st, v.astype(np.float64)
+
+
+def lens_dev(lens):
+    if lens is None:
+        return None
+    return torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+
+
+def gpu_sdpa(dtype):
+    """sdpa_fn for the pins: rounds inputs to ``dtype`` and runs mha_sdpa.
+    Returns (fn, rnd) where rnd rounds an array the same way."""
+    def rnd(x):
+        return rounded(x, dtype)[1]
+
+    def fn(Q, K, V, scale, mask, lens):
+        Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
+        B, h, n_q, d = Q.shape
+        n_k, d_v = K.shape[2], V.shape[3]
+        dpad = 64 if dtype != "f32" else max(16, 1 << max(0, (max(d, d_v) - 1)).bit_length())
+        # the pins use small head dims: zero-pad q/k (scores unchanged) and v
+        # (extra output columns dropped)
+        Qp = np.zeros((B, h, n_q, dpad)); Qp[..., :d] = Q
+        Kp = np.zeros((B, h, n_k, dpad)); Kp[..., :d] = K
+        Vp = np.zeros((B, h, n_k, dpad)); Vp[..., :d_v] = V
+        tq, tk, tv = (to_dev(rounded(a, dtype)[0], dtype) for a in (Qp, Kp, Vp))
+        out = libmha.sdpa(tq, tk, tv, scale=scale, mask=mask, seq_lens=lens_dev(lens))
+        torch.cuda.synchronize()
+        return from_dev(out)[..., :d_v]
+    return fn, rnd

@@ -225,11 +225,17 @@ def pin_one_hot(sdpa_fn, atol=1e-9, rnd=_ident, d=8):
     Q = rnd(_rand(rs, B, h, nq, d))
     K = rnd(_rand(rs, B, h, nk, d))
     V = rnd(_rand(rs, B, h, nk, d))
-    s = np.einsum("bhqd,bhkd->bhqk", Q, K)
-    srt = np.sort(s, axis=-1)
-    margin = float((srt[..., -1] - srt[..., -2]).min())
-    c = 60.0 / max(margin, 1e-3)      # margin·c ≥ 60 → the runner-up gets ≤ e^-60
-    O = np.asarray(sdpa_fn(Q, K * c, V, 1.0, NONE, None))
+    c = 1.0
+    while True:   # grow the key scale until every row's winner leads by ≥ 60
+        Kc = rnd(K * c)
+        s = np.einsum("bhqd,bhkd->bhqk", Q, Kc)
+        srt = np.sort(s, axis=-1)
+        margin = float((srt[..., -1] - srt[..., -2]).min())
+        if margin >= 60.0 or c > 1e6:
+            break
+        c *= 2.0
+    assert margin >= 60.0
+    O = np.asarray(sdpa_fn(Q, Kc, V, 1.0, NONE, None))
     best = np.argmax(s, axis=-1)                         # [B, h, nq]
     exp = np.stack([[V[b, i][best[b, i]] for i in range(h)] for b in range(B)])
     _close(O, exp, atol, "one-hot limit")

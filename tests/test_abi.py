@@ -1,0 +1,132 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the host before touching a device.
+
+No call here reaches a kernel launch: every call either fails validation or
+is a zero-size no-op, both of which return before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_head_scaled_amd import libmha as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mha.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(M.LIB_PATH), reason="libmha.so not built")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mha_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_api():
+    assert declared_functions() == sorted(M.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    L = ctypes.CDLL(M.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), f"libmha.so does not export {name}"
+
+
+def test_status_strings_and_version():
+    assert M.status_string(M.MHA_OK) == "MHA_OK"
+    for code in range(-7, 0):
+        s = M.status_string(code)
+        assert s.startswith("MHA_ERR_"), s
+    assert "unknown" in M.status_string(-99)
+    assert M.version() == 100
+
+
+def _sdpa(dtype=M.MHA_BF16, B=1, h=1, n_q=8, n_k=8, d_k=64, d_v=64, scale=0.125,
+          mask=M.MHA_MASK_NONE, Q=0x1000, K=0x100000, V=0x200000, O=0x300000, lens=None):
+    L = M.lib()
+    return L.mha_sdpa(Q, K, V, O, dtype, B, h, n_q, n_k, d_k, d_v, scale, mask, lens, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), M.MHA_ERR_DTYPE),
+    (dict(mask=3), M.MHA_ERR_INVALID_ARG),
+    (dict(B=-1), M.MHA_ERR_SHAPE),
+    (dict(d_k=0), M.MHA_ERR_SHAPE),
+    (dict(n_k=9, mask=M.MHA_MASK_CAUSAL), M.MHA_ERR_SHAPE),
+    (dict(scale=float("nan")), M.MHA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), M.MHA_ERR_INVALID_ARG),
+    (dict(d_k=128, d_v=128), M.MHA_ERR_UNSUPPORTED),
+    (dict(d_k=64, d_v=32), M.MHA_ERR_UNSUPPORTED),
+    (dict(dtype=M.MHA_F32, d_k=48, d_v=48), M.MHA_ERR_UNSUPPORTED),
+    (dict(Q=None), M.MHA_ERR_INVALID_ARG),
+    (dict(O=None), M.MHA_ERR_INVALID_ARG),
+    (dict(V=None), M.MHA_ERR_INVALID_ARG),
+    (dict(O=0x1000 + 64), M.MHA_ERR_ALIAS),        # O overlaps Q
+    (dict(O=0x200000 - 16), M.MHA_ERR_ALIAS),      # O's tail runs into V
+    (dict(n_q=1 << 31), M.MHA_ERR_SHAPE),
+    (dict(K=0x100000 + 8), M.MHA_ERR_INVALID_ARG),  # not 16-byte aligned
+    (dict(lens=0x900002), M.MHA_ERR_INVALID_ARG),
+])
+def test_sdpa_rejects(kw, code):
+    assert _sdpa(**kw) == code
+    assert M.last_error() != ""
+
+
+def test_sdpa_alias_edges():
+    # O (8 rows x 64 bf16 = 1024 bytes) starting 1008 bytes before K: its
+    # last 16 bytes are K's first 16; ending exactly at K is no overlap
+    assert _sdpa(O=0x100000 - 8 * 64 * 2 + 16) == M.MHA_ERR_ALIAS
+
+
+def test_zero_sizes_are_noops():
+    for kw in (dict(B=0), dict(h=0), dict(n_q=0), dict(B=0, Q=None, O=None)):
+        assert _sdpa(**kw) == M.MHA_OK
+
+
+def _fwd(dtype=M.MHA_BF16, B=2, n_q=8, n_k=8, d_model=128, h=2, mask=M.MHA_MASK_NONE,
+         x_q=0x1000, x_kv=None, W=(0x100000, 0x200000, 0x300000, 0x400000), out=0x500000,
+         lens=None, ws=None, ws_bytes=0):
+    L = M.lib()
+    return L.mha_forward(x_q, x_kv, W[0], W[1], W[2], W[3], out, dtype, B, n_q, n_k, d_model, h,
+                         mask, lens, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), M.MHA_ERR_DTYPE),
+    (dict(dtype=M.MHA_F32), M.MHA_ERR_UNSUPPORTED),
+    (dict(d_model=129, h=2), M.MHA_ERR_SHAPE),
+    (dict(d_model=256, h=2), M.MHA_ERR_UNSUPPORTED),     # head dim 128
+    (dict(h=0), M.MHA_ERR_SHAPE),
+    (dict(n_k=9), M.MHA_ERR_SHAPE),                       # self-attention, n_k != n_q
+    (dict(n_k=9, x_kv=0x600000, mask=M.MHA_MASK_CAUSAL), M.MHA_ERR_SHAPE),
+    (dict(mask=9), M.MHA_ERR_INVALID_ARG),
+    (dict(x_q=None), M.MHA_ERR_INVALID_ARG),
+    (dict(W=(0x100000, None, 0x300000, 0x400000)), M.MHA_ERR_INVALID_ARG),
+    (dict(ws=0x700000, ws_bytes=16), M.MHA_ERR_WORKSPACE),
+    (dict(ws=0x700010, ws_bytes=1 << 20), M.MHA_ERR_INVALID_ARG),   # misaligned workspace
+    (dict(out=0x1000), M.MHA_ERR_ALIAS),
+    (dict(out=0x400000 + 16), M.MHA_ERR_ALIAS),
+    (dict(ws=0x500000, ws_bytes=1 << 20), M.MHA_ERR_ALIAS),
+    (dict(out=0x500008), M.MHA_ERR_INVALID_ARG),   # not 16-byte aligned
+])
+def test_forward_rejects(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_forward_zero_sizes_are_noops():
+    assert _fwd(B=0) == M.MHA_OK
+    assert _fwd(n_q=0, n_k=0) == M.MHA_OK
+
+
+def test_workspace_size():
+    L = M.lib()
+    B, n_q, n_k, dm, h = 8, 384, 512, 1024, 16
+    need = L.mha_forward_workspace_size(B, n_q, n_k, dm, h, M.MHA_BF16)
+    assert need >= 2 * (2 * B * n_q * dm + 2 * B * n_k * dm)
+    assert need % 256 == 0
+    assert need < 2 * (2 * B * n_q * dm + 2 * B * n_k * dm) + 4 * 256
+    assert L.mha_forward_workspace_size(B, n_q, n_k, dm, 0, M.MHA_BF16) == 0
+    assert L.mha_forward_workspace_size(B, n_q, n_k, 1000, 16, M.MHA_BF16) == 0

@@ -1,0 +1,161 @@
+"""mha_forward on the GPU against the fp64 oracle (max-abs 2e-2).
+
+The projections are rounded to the input dtype before attention and the
+concat before W^O (one rounding each, as any bf16 pipeline does); the
+tolerance covers those roundings.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import TOL, from_dev, lens_dev, note, require_gpu, rounded, to_dev, torch
+import pins
+from transformer_head_scaled_amd import libmha, synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _check(got, exp, dtype, what):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(got - exp)))
+    print(f"[parity] {what}: max-abs {err:.3e} (tol {TOL[dtype]:.0e}), max|out| {np.abs(exp).max():.2f}",
+          flush=True)
+    assert err <= TOL[dtype], f"{what}: max-abs {err:.3e} > {TOL[dtype]}"
+
+
+def _run(ins, dtype, h, mask="none", lens=None, workspace=False):
+    dev = {k: to_dev(v[0], dtype) for k, v in ins.items()}
+    ws = None
+    if workspace:
+        B, n_q, dm = dev["x_q"].shape
+        n_k = dev["x_kv"].shape[1] if "x_kv" in dev else n_q
+        code = {"bf16": libmha.MHA_BF16, "f16": libmha.MHA_F16}[dtype]
+        ws = torch.empty(libmha.workspace_size(B, n_q, n_k, dm, h, code), dtype=torch.uint8,
+                         device="cuda")
+    out = libmha.forward(dev["x_q"], dev["Wq"], dev["Wk"], dev["Wv"], dev["Wo"], h,
+                         x_kv=dev.get("x_kv"), mask=mask, kv_lens=lens_dev(lens), workspace=ws)
+    torch.cuda.synchronize()
+    return from_dev(out)
+
+
+def _oracle(ins, h, mask="none", lens=None):
+    mk = oracle.MASK_CAUSAL if mask == "causal" else oracle.MASK_NONE
+    x_kv = ins["x_kv"][1] if "x_kv" in ins else None
+    return oracle.mha(ins["x_q"][1], x_kv, ins["Wq"][1], ins["Wk"][1], ins["Wv"][1], ins["Wo"][1],
+                      h, mk, lens)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("workspace", [True, False])
+def test_workload_base_encoder_keypad(dtype, workspace):
+    """Base-model encoder self-attention: B=32, n=64, d_model=512, h=8,
+    key lengths uniform in [16, 64]."""
+    ins, lens = synth.workload_inputs(2, dtype=dtype)
+    note(f"forward {dtype} base encoder keypad ws={workspace}")
+    got = _run(ins, dtype, 8, "none", lens, workspace)
+    _check(got, _oracle(ins, 8, "none", lens), dtype, f"base encoder {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_workload_big_cross(dtype):
+    """Big-model encoder-decoder attention: B=8, n_q=384, n_k=512,
+    d_model=1024, h=16."""
+    ins, _ = synth.workload_inputs(4, dtype=dtype)
+    note(f"forward {dtype} big cross")
+    got = _run(ins, dtype, 16, "none", None, True)
+    _check(got, _oracle(ins, 16), dtype, f"big cross {dtype}")
+
+
+@pytest.mark.parametrize("case", [
+    # (B, n_q, n_k, d_model, h, cross, mask, lens)
+    (2, 100, 100, 512, 8, False, "causal", None),        # decoder self-attention
+    (3, 77, 77, 256, 4, False, "causal", [77, 5, 0]),
+    (2, 33, 190, 512, 8, True, "none", [190, 1]),
+    (1, 1, 1, 64, 1, False, "none", None),              # h = 1, d_model = 64
+    (4, 130, 70, 128, 2, True, "none", None),
+])
+def test_ragged(case):
+    B, n_q, n_k, dm, h, cross, mask, lens = case
+    dtype = "bf16"
+    ins = synth.mha_inputs(200 + n_q, B, n_q, n_k, dm, h, cross, dtype=dtype)
+    note(f"forward ragged {case}")
+    got = _run(ins, dtype, h, mask, lens, True)
+    _check(got, _oracle(ins, h, mask, lens), dtype, f"ragged {case}")
+
+
+def test_single_head_equals_sdpa_chain():
+    """h = 1 (Table 3 (A) of the nickwang.xyz page): one head of full width
+    d_k = d_model, so the sublayer is one attention with scale 1/√d_model
+    followed by W^O."""
+    def mha_fn(x_q, x_kv, Wq, Wk, Wv, Wo, h, mask, lens):
+        ins = {"x_q": rounded(x_q, "bf16"), "Wq": rounded(Wq, "bf16"), "Wk": rounded(Wk, "bf16"),
+               "Wv": rounded(Wv, "bf16"), "Wo": rounded(Wo, "bf16")}
+        if x_kv is not None:
+            ins["x_kv"] = rounded(x_kv, "bf16")
+        return _run(ins, "bf16", h, "causal" if mask else "none", lens, True)
+
+    rs = np.random.default_rng(5)
+    B, n, dm = 2, 40, 64
+    x = rs.standard_normal((B, n, dm))
+    W = [rs.standard_normal((dm, dm)) / 8 for _ in range(4)]
+    xr = rounded(x, "bf16")[1]
+    Wr = [rounded(w, "bf16")[1] for w in W]
+    note("forward h=1 vs sdpa chain")
+    got = mha_fn(x, None, *W, 1, 0, None)
+    Q, K, V = ((xr @ w)[:, None] for w in Wr[:3])
+    o = oracle.sdpa(Q, K, V, 1 / np.sqrt(dm))[:, 0]
+    _check(got, o @ Wr[3], "bf16", "h=1 chain")
+
+
+def test_head_relabelling_invariance():
+    """Permuting head blocks of Wq/Wk/Wv (columns) and Wo (rows) together
+    leaves the library's output unchanged (up to rounding order)."""
+    dtype = "bf16"
+    ins = synth.mha_inputs(31, 2, 96, 96, 512, 8, False, dtype=dtype)
+    perm = [3, 1, 7, 0, 5, 2, 6, 4]
+    cols = np.concatenate([np.arange(p * 64, (p + 1) * 64) for p in perm])
+    insp = dict(ins)
+    for k in ("Wq", "Wk", "Wv"):
+        insp[k] = (np.ascontiguousarray(ins[k][0][:, cols]), ins[k][1][:, cols])
+    insp["Wo"] = (np.ascontiguousarray(ins["Wo"][0][cols, :]), ins["Wo"][1][cols, :])
+    note("forward head relabelling")
+    a = _run(ins, dtype, 8, "causal", None, True)
+    b = _run(insp, dtype, 8, "causal", None, True)
+    _check(b, a, dtype, "head relabelling")
+
+
+def test_out_guard_band_and_workspace_reuse():
+    dtype = "bf16"
+    B, n, dm, h = 3, 50, 256, 4
+    ins = synth.mha_inputs(41, B, n, n, dm, h, False, dtype=dtype)
+    dev = {k: to_dev(v[0], dtype) for k, v in ins.items()}
+    pad = 2048
+    buf = torch.full((pad + B * n * dm + pad,), 3.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[pad:pad + B * n * dm].view(B, n, dm)
+    ws = torch.empty(libmha.workspace_size(B, n, n, dm, h, libmha.MHA_BF16), dtype=torch.uint8,
+                     device="cuda")
+    note("forward guard band")
+    for _ in range(2):
+        libmha.forward(dev["x_q"], dev["Wq"], dev["Wk"], dev["Wv"], dev["Wo"], h, out=out,
+                       workspace=ws, mask="causal")
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 3.0) and torch.all(buf[-pad:] == 3.0)
+    _check(from_dev(out), _oracle(ins, h, "causal"), dtype, "guard band")
+
+
+def test_mha_pins_through_api():
+    """The oracle's multi-head pins re-run through the library."""
+    def mha_fn(x_q, x_kv, Wq, Wk, Wv, Wo, h, mask, lens):
+        ins = {"x_q": rounded(x_q, "bf16"), "Wq": rounded(Wq, "bf16"), "Wk": rounded(Wk, "bf16"),
+               "Wv": rounded(Wv, "bf16"), "Wo": rounded(Wo, "bf16")}
+        if x_kv is not None:
+            ins["x_kv"] = rounded(x_kv, "bf16")
+        return _run(ins, "bf16", h, "causal" if mask else "none", lens, True)
+    note("mha pins via API")
+    pins.pin_mha_shapes(mha_fn)

@@ -1,0 +1,278 @@
+"""mha_sdpa on the GPU against the fp64 oracle, element by element.
+
+Tolerance (max-abs): 2e-2 for bf16/fp16 inputs, 1e-5 for the fp32 path.
+Sizes span several tiles with ragged tails; the full-size long-sequence
+workload is checked on whole sampled heads plus sampled rows of every head
+(each sampled causal row r against the unmasked attention of q_r over keys
+0..r, the reduction the pins establish for the oracle).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import (TOL, from_dev, gpu_sdpa, lens_dev, note, require_gpu, rounded, to_dev,
+                      torch)
+import pins
+from transformer_head_scaled_amd import libmha, synth
+
+pytestmark = pytest.mark.gpu
+
+MASKS = {"none": oracle.MASK_NONE, "causal": oracle.MASK_CAUSAL}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _run(ins, dtype, mask, lens=None, scale=0.125):
+    tq, tk, tv = (to_dev(ins[n][0], dtype) for n in "QKV")
+    out = libmha.sdpa(tq, tk, tv, scale=scale, mask=mask, seq_lens=lens_dev(lens))
+    torch.cuda.synchronize()
+    return from_dev(out)
+
+
+def _check(got, exp, dtype, what):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(got - exp))) if got.size else 0.0
+    print(f"[parity] {what}: max-abs {err:.3e} (tol {TOL[dtype]:.0e})", flush=True)
+    assert err <= TOL[dtype], f"{what}: max-abs {err:.3e} > {TOL[dtype]}"
+
+
+def test_workload_f32_single_head():
+    """[1,1,16,64] fp32, no mask, scale 1/8: the 1e-5 parity case."""
+    w = synth.WORKLOADS[1]
+    ins = synth.sdpa_inputs(1, w["B"], w["h"], w["n_q"], w["n_k"], w["d"], dtype="f32")
+    note("sdpa f32 [1,1,16,64]")
+    got = _run(ins, "f32", "none")
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], 0.125)
+    _check(got, exp, "f32", "f32 [1,1,16,64]")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_workload_causal_b16_n512(dtype):
+    """[16,8,512,64] causal (decoder self-attention), all outputs."""
+    ins = synth.sdpa_inputs(3, 16, 8, 512, 512, 64, dtype=dtype)
+    note(f"sdpa {dtype} causal [16,8,512,64]")
+    got = _run(ins, dtype, "causal")
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], 0.125, oracle.MASK_CAUSAL)
+    _check(got, exp, dtype, f"{dtype} causal [16,8,512,64]")
+
+
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_workload_long_b4_n4096_sampled(mask):
+    """[4,8,4096,64], the launch the bench times: two whole heads, plus 12
+    sampled rows (first, last, random) of every head."""
+    dtype = "bf16"
+    ins = synth.sdpa_inputs(5, 4, 8, 4096, 4096, 64, dtype=dtype)
+    note(f"sdpa bf16 {mask} [4,8,4096,64]")
+    got = _run(ins, dtype, mask)
+    Q, K, V = (ins[n][1] for n in "QKV")
+    mk = MASKS[mask]
+    for (b, i) in ((0, 0), (3, 7)):
+        exp, _ = oracle.attention_head(Q[b, i], K[b, i], V[b, i], 0.125, mk)
+        _check(got[b, i], exp, dtype, f"{mask} head ({b},{i}) all rows")
+    rs = np.random.default_rng(55)
+    rows = np.concatenate([[0, 1, 63, 64, 4095], rs.integers(0, 4096, size=7)])
+    err = 0.0
+    for b in range(4):
+        for i in range(8):
+            for r in rows:
+                top = r + 1 if mask == "causal" else 4096
+                exp, _ = oracle.attention_head(Q[b, i, r:r + 1], K[b, i, :top], V[b, i, :top], 0.125)
+                err = max(err, float(np.max(np.abs(got[b, i, r] - exp[0]))))
+    print(f"[parity] {mask} sampled rows of all heads: max-abs {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+
+
+# ragged shapes: tails of the 128-row query blocks and 64-key tiles, tiny
+# sizes, cross-attention n_q != n_k, key padding including 0 and > n_k
+RAGGED = [
+    # (B, h, n_q, n_k, mask, lens)
+    (1, 1, 1, 1, "none", None),
+    (2, 3, 1, 77, "none", None),
+    (1, 2, 33, 33, "causal", None),
+    (2, 2, 129, 129, "causal", None),
+    (3, 1, 200, 200, "causal", [0, 150, 999]),
+    (2, 2, 100, 300, "none", [1, 300]),
+    (1, 4, 257, 65, "none", None),
+    (2, 1, 64, 64, "none", [64, 17]),
+    (1, 1, 384, 512, "none", None),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "x".join(map(str, c[:4])) + f"_{c[4]}" + ("_lens" if c[5] else ""))
+def test_ragged(dtype, case):
+    B, h, n_q, n_k, mask, lens = case
+    ins = synth.sdpa_inputs(100 + n_q, B, h, n_q, n_k, 64, dtype=dtype)
+    note(f"sdpa {dtype} ragged {case}")
+    got = _run(ins, dtype, mask, lens)
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], 0.125, MASKS[mask], lens)
+    _check(got, exp, dtype, f"{dtype} {case}")
+
+
+@pytest.mark.parametrize("d", [16, 32, 128])
+def test_f32_head_dims(d):
+    ins = synth.sdpa_inputs(7, 2, 2, 70, 45, d, dtype="f32")
+    note(f"sdpa f32 d={d}")
+    got = _run(ins, "f32", "none", [45, 12], scale=1 / math.sqrt(d))
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], 1 / math.sqrt(d), oracle.MASK_NONE, [45, 12])
+    _check(got, exp, "f32", f"f32 d={d}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 1.0])
+def test_unusual_scales(dtype, scale):
+    """A negative scale (the kernel negates Q exactly), scale 0 (uniform
+    weights) and an unscaled softmax."""
+    ins = synth.sdpa_inputs(8, 2, 2, 130, 130, 64, dtype=dtype)
+    note(f"sdpa {dtype} scale={scale}")
+    for mask in ("none", "causal"):
+        got = _run(ins, dtype, mask, [130, 61], scale=scale)
+        exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], scale, MASKS[mask], [130, 61])
+        _check(got, exp, dtype, f"{dtype} scale={scale} {mask}")
+
+
+# ---- the oracle's pins, re-run through the library
+
+GPU_PINS = [pins.pin_rows_sum_to_one, pins.pin_zero_query_is_mean, pins.pin_causal_row0,
+            pins.pin_permutation, pins.pin_one_hot, pins.pin_mask_reduces,
+            pins.pin_masked_contents_ignored]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("pin", GPU_PINS, ids=lambda p: p.__name__)
+def test_pin_through_api(pin, dtype):
+    fn, rnd = gpu_sdpa(dtype)
+    note(f"pin {pin.__name__} {dtype}")
+    kw = {"rnd": rnd}
+    if pin in (pins.pin_causal_row0, pins.pin_masked_contents_ignored):
+        kw["atol"] = 0.0          # exact: row 0 sees one key; masked rows never read
+    else:
+        kw["atol"] = TOL[dtype]
+    pin(fn, **kw)
+
+
+def test_pin_rows_sum_long():
+    fn, rnd = gpu_sdpa("bf16")
+    note("pin rows-sum-to-one long")
+    pins.pin_rows_sum_to_one(fn, atol=TOL["bf16"], rnd=rnd,
+                             shapes=((1, 2, 1000, 1000, 64), (2, 1, 300, 700, 64)))
+
+
+def test_empty_rows():
+    for dtype in ("bf16", "f32"):
+        fn, _ = gpu_sdpa(dtype)
+        note(f"pin empty rows {dtype}")
+        pins.pin_empty_rows(fn)
+
+
+def test_worked_example_fp32():
+    """The printed worked example (query "il", seven 2-d keys, scale 1/√2)
+    reproduced at its printed precision through the fp32 path, with and
+    without the causal toggle."""
+    fn, _ = gpu_sdpa("f32")
+    note("worked example f32")
+    pins.pin_worked_example(fn)
+    pins.pin_worked_example_causal(fn)
+
+
+def test_worked_example_bf16_vs_oracle():
+    """The same example through the bf16 MFMA path (q, k zero-padded to 64):
+    equal to the oracle on the bf16-rounded inputs within 2e-2."""
+    g = pins.worked_example()
+    n = len(g["keys"])
+    Q = np.zeros((1, 1, n, 64))
+    K = np.zeros((1, 1, n, 64))
+    Q[0, 0, :, :2] = g["query"]
+    K[0, 0, :, :2] = g["keys"]
+    V = np.zeros((1, 1, n, 64))
+    V[0, 0, :, :n] = np.eye(n)
+    fn, rnd = gpu_sdpa("bf16")
+    note("worked example bf16")
+    for mask in (oracle.MASK_NONE, oracle.MASK_CAUSAL):
+        got = fn(Q, K, V, g["scale"], mask, None)
+        exp = oracle.sdpa(rnd(Q), rnd(K), rnd(V), g["scale"], mask)
+        _check(got, exp, "bf16", f"worked example mask={mask}")
+
+
+def test_saturation_fp32():
+    """σ(8) and σ(1) of the saturation example, through the fp32 path."""
+    fn, _ = gpu_sdpa("f32")
+    d = 64
+    Q = np.zeros((1, 1, 1, d)); Q[0, 0, 0, 0] = 8.0
+    K = np.zeros((1, 1, 2, d)); K[0, 0, 0, 0] = 1.0; K[0, 0, 1, 1] = 1.0
+    V = np.zeros((1, 1, 2, d)); V[0, 0, 0, 0] = 1.0; V[0, 0, 1, 1] = 1.0
+    sig = lambda x: 1 / (1 + math.exp(-x))  # noqa: E731
+    note("saturation f32")
+    p = fn(Q, K, V, 1.0, oracle.MASK_NONE, None)[0, 0, 0, :2]
+    np.testing.assert_allclose(p, [sig(8), sig(-8)], atol=1e-6)
+    p = fn(Q, K, V, 0.125, oracle.MASK_NONE, None)[0, 0, 0, :2]
+    np.testing.assert_allclose(p, [sig(1), sig(-1)], atol=1e-6)
+
+
+def test_shift_and_linearity_exact_grid():
+    """Softmax shift invariance and linearity in V through the bf16 path,
+    on inputs whose shifted / combined values are exactly representable in
+    bf16 (multiples of 1/8 and 1/16 of small magnitude)."""
+    rs = np.random.default_rng(77)
+    B, h, n, d = 2, 2, 150, 64
+    Q = rs.integers(-8, 9, size=(B, h, n, d)) / 32.0
+    K = rs.integers(-16, 17, size=(B, h, n, d)) / 8.0
+    V1 = rs.integers(-8, 9, size=(B, h, n, d)) / 4.0
+    V2 = rs.integers(-8, 9, size=(B, h, n, d)) / 4.0
+    u = np.full(d, 4.0)
+    fn, rnd = gpu_sdpa("bf16")
+    for arr in (Q, K, K + u, V1, V2, 0.75 * V1 - 2.5 * V2):
+        assert np.array_equal(rnd(arr), arr)
+    note("shift/linearity bf16")
+    for mask in (oracle.MASK_NONE, oracle.MASK_CAUSAL):
+        O = fn(Q, K, V1, 0.125, mask, None)
+        Os = fn(Q, K + u, V1, 0.125, mask, None)
+        _check(Os, O, "bf16", f"shift invariance mask={mask}")
+        O2 = fn(Q, K, V2, 0.125, mask, None)
+        O12 = fn(Q, K, 0.75 * V1 - 2.5 * V2, 0.125, mask, None)
+        _check(O12, 0.75 * O - 2.5 * O2, "bf16", f"linearity mask={mask}")
+
+
+def test_causal_row0_bit_exact_full_size():
+    """Causal row 0 is V[0] exactly, at the long-sequence size."""
+    ins = synth.sdpa_inputs(5, 4, 8, 4096, 4096, 64, dtype="bf16")
+    note("causal row0 [4,8,4096,64]")
+    tq, tk, tv = (to_dev(ins[n][0], "bf16") for n in "QKV")
+    out = libmha.sdpa(tq, tk, tv, scale=0.125, mask="causal")
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, :, 0, :], tv[:, :, 0, :])
+
+
+def test_repeatable_bitwise():
+    """Fixed reduction order, no atomics: two runs are bitwise equal."""
+    ins = synth.sdpa_inputs(9, 2, 8, 1000, 1000, 64, dtype="bf16")
+    tq, tk, tv = (to_dev(ins[n][0], "bf16") for n in "QKV")
+    note("repeatability bf16 [2,8,1000,64]")
+    for mask in ("none", "causal"):
+        a = libmha.sdpa(tq, tk, tv, mask=mask)
+        b = libmha.sdpa(tq, tk, tv, mask=mask)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+def test_output_guard_band():
+    """The kernel writes exactly O: canary regions before and after it in
+    the same allocation stay untouched."""
+    B, h, n, d = 2, 3, 77, 64
+    ins = synth.sdpa_inputs(10, B, h, n, n, d, dtype="bf16")
+    tq, tk, tv = (to_dev(ins[n_][0], "bf16") for n_ in "QKV")
+    pad = 4096
+    buf = torch.full((pad + B * h * n * d + pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[pad:pad + B * h * n * d].view(B, h, n, d)
+    note("guard band")
+    libmha.sdpa(tq, tk, tv, mask="causal", out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 7.0) and torch.all(buf[-pad:] == 7.0)
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], 0.125, oracle.MASK_CAUSAL)
+    _check(from_dev(out), exp, "bf16", "guard band output")

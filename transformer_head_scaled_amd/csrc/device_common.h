@@ -1,0 +1,85 @@
+// Device-side helpers shared by the libmha kernels (gfx950 / CDNA4 only).
+//
+// Vector types for the 32x32x16 MFMA operands, raw 16-byte LDS/global
+// words, dtype tags and conversions.  Nothing here computes attention.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mha {
+
+enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// D(32x32, fp32) += A(32x16) * B(16x32); 8 half-precision values per lane.
+// Operand layout (lane l, element j): A[row l%32][k 8*(l/32)+j],
+// B[k 8*(l/32)+j][col l%32].  Result (lane l, element i):
+// D[row 8*(i/4) + 4*(l/32) + i%4][col l%32].
+template <int DT>
+__device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (DT == DT_BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// Two fp32 values -> one dword holding two half-precision values (RNE),
+// low half = a.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (DT == DT_BF16) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// Sign bit of each 16-bit lane of a packed word (used to negate operands
+// exactly).
+__device__ __forceinline__ u32x4 flip_signs(u32x4 v) {
+  const uint32_t s = 0x80008000u;
+  return u32x4{v[0] ^ s, v[1] ^ s, v[2] ^ s, v[3] ^ s};
+}
+
+// Combine a value with the one held by the lane 32 positions away
+// (lane l and lane l^32).  v_permlane32_swap exchanges the upper half of
+// one register with the lower half of the other; applied to two copies of
+// x it leaves x's lower half in one result and its upper half in the
+// other, in every lane, so max/sum of the two is the pair's max/sum.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Map the hardware workgroup index onto a logical tile index so that
+// consecutive logical tiles run on the same XCD (workgroups are dealt to
+// the 8 XCDs round-robin; each XCD has its own L2).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t hw, uint32_t total) {
+  const uint32_t nx = 8;
+  const uint32_t xcd = hw % nx, slot = hw / nx;
+  const uint32_t per = total / nx, extra = total % nx;
+  return xcd * per + (xcd < extra ? xcd : extra) + slot;
+}
+
+}  // namespace mha

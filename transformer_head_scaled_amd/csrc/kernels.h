@@ -1,0 +1,59 @@
+// Internal interface between the libmha host layer and its HIP kernels.
+// Not part of the public C ABI (that is include/mha.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mha {
+
+// Key tile (keys per LDS stage) and query blocks of 32 rows per wave of the
+// bf16/fp16 attention kernel.  One workgroup covers 4 * 32 * kSdpaQB rows.
+constexpr int kSdpaBN = 64;
+constexpr int kSdpaQB = 1;
+
+// Strides are in elements.  Q/K/V/O rows are d contiguous elements.
+struct SdpaArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  int64_t q_sb, q_sh, q_sr;
+  int64_t k_sb, k_sh, k_sr;
+  int64_t v_sb, v_sh, v_sr;
+  int64_t o_sb, o_sh, o_sr;
+  int32_t B, H, n_q, n_k;
+  float c;              // |scale| * log2(e)   (MFMA path)
+  int32_t neg;          // scale < 0: the MFMA path negates Q exactly
+  const int32_t* lens;  // device int32[B] valid key counts, or null
+};
+
+hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float scale, hipStream_t st);
+int sdpa_rows_per_workgroup(int dtype);
+
+// One GEMM C = A·W of the projections: A [M, K] row-major (row stride lda),
+// W [K, N] row-major (row stride ldw).  Output element (m, n) is written to
+//   C + (m / rows_per_b) * c_sb + (m % rows_per_b) * c_st
+//     + (n / head_dim) * c_sh + (n % head_dim)
+// which expresses both the head-split layout [B, h, n, d] and a plain
+// row-major [M, N] matrix.
+struct GemmProblem {
+  const void* A;
+  const void* W;
+  void* C;
+  int64_t lda, ldw;
+  int64_t c_sb, c_st, c_sh;
+  int32_t M, rows_per_b, head_dim, pad_;
+};
+
+struct GemmArgs {
+  GemmProblem prob[3];
+  int32_t nprob;
+  int32_t N, K;
+  int32_t pad_;
+};
+
+// Chooses the tile shape from the problem sizes.
+hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t st);
+
+}  // namespace mha

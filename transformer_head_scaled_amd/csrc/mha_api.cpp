@@ -1,0 +1,303 @@
+// libmha host layer: argument validation, workspace layout, dispatch.
+//
+// Implements the C ABI declared in include/mha.h.  Every check runs before
+// the first enqueue, so an error never leaves partial output.
+
+#include "mha.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MHA_OK;
+}
+
+bool trace_on() {
+  static const int on = [] {
+    const char* e = std::getenv("MHA_TRACE");
+    return (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+size_t elem_size(int dtype) { return dtype == MHA_F32 ? 4 : 2; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+bool overlap(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+constexpr int64_t kMaxRows = (int64_t)1 << 30;  // rows per sequence (int32 indexing in kernels)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t q, k, v, concat, total;
+};
+
+WsLayout ws_layout(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model, int dtype) {
+  const size_t es = elem_size(dtype);
+  WsLayout w;
+  w.q = 0;
+  w.k = align256(w.q + (size_t)(B * n_q * d_model) * es);
+  w.v = align256(w.k + (size_t)(B * n_k * d_model) * es);
+  w.concat = align256(w.v + (size_t)(B * n_k * d_model) * es);
+  w.total = align256(w.concat + (size_t)(B * n_q * d_model) * es);
+  return w;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mha_status_string(int status) {
+  switch (status) {
+    case MHA_OK: return "MHA_OK";
+    case MHA_ERR_INVALID_ARG: return "MHA_ERR_INVALID_ARG: invalid argument";
+    case MHA_ERR_SHAPE: return "MHA_ERR_SHAPE: inconsistent or out-of-range sizes";
+    case MHA_ERR_DTYPE: return "MHA_ERR_DTYPE: unknown dtype";
+    case MHA_ERR_UNSUPPORTED: return "MHA_ERR_UNSUPPORTED: valid but not implemented";
+    case MHA_ERR_WORKSPACE: return "MHA_ERR_WORKSPACE: workspace too small";
+    case MHA_ERR_ALIAS: return "MHA_ERR_ALIAS: output overlaps an input";
+    case MHA_ERR_HIP: return "MHA_ERR_HIP: HIP runtime error";
+    default: return "unknown libmha status";
+  }
+}
+
+const char* mha_last_error(void) { return g_err; }
+
+int mha_version(void) { return 100; }
+
+int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype, int64_t B,
+             int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, float scale,
+             int32_t mask_kind, const int32_t* seq_lens, void* stream) {
+  if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16)
+    return fail(MHA_ERR_DTYPE, "mha_sdpa: dtype %d", (int)dtype);
+  if (mask_kind != MHA_MASK_NONE && mask_kind != MHA_MASK_CAUSAL)
+    return fail(MHA_ERR_INVALID_ARG, "mha_sdpa: mask_kind %d", (int)mask_kind);
+  if (B < 0 || h < 0 || n_q < 0 || n_k < 0 || d_k <= 0 || d_v <= 0)
+    return fail(MHA_ERR_SHAPE, "mha_sdpa: negative or zero size");
+  if (n_q > kMaxRows || n_k > kMaxRows || B > 65535 || h > 65535 || B * h > (int64_t)1 << 24)
+    return fail(MHA_ERR_SHAPE, "mha_sdpa: size beyond the supported range");
+  if (mask_kind == MHA_MASK_CAUSAL && n_q != n_k)
+    return fail(MHA_ERR_SHAPE, "mha_sdpa: causal mask needs n_q == n_k (%lld vs %lld)",
+                (long long)n_q, (long long)n_k);
+  if (!std::isfinite(scale)) return fail(MHA_ERR_INVALID_ARG, "mha_sdpa: scale is not finite");
+  if (dtype == MHA_F32) {
+    if (d_k != d_v || (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128))
+      return fail(MHA_ERR_UNSUPPORTED, "mha_sdpa: f32 needs d_k == d_v in {16,32,64,128}");
+  } else if (d_k != 64 || d_v != 64) {
+    return fail(MHA_ERR_UNSUPPORTED, "mha_sdpa: bf16/f16 needs d_k == d_v == 64");
+  }
+  if (B == 0 || h == 0 || n_q == 0) return ok();
+  if (!Q || !O || ((!K || !V) && n_k > 0))
+    return fail(MHA_ERR_INVALID_ARG, "mha_sdpa: null tensor pointer");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3) != 0)
+    return fail(MHA_ERR_INVALID_ARG, "mha_sdpa: tensors must be 16-byte aligned");
+  const size_t es = elem_size(dtype);
+  const Range ro = range_of(O, (size_t)(B * h * n_q * d_v) * es);
+  if (overlap(ro, range_of(Q, (size_t)(B * h * n_q * d_k) * es)) ||
+      overlap(ro, range_of(K, (size_t)(B * h * n_k * d_k) * es)) ||
+      overlap(ro, range_of(V, (size_t)(B * h * n_k * d_v) * es)) ||
+      (seq_lens && overlap(ro, range_of(seq_lens, (size_t)B * 4))))
+    return fail(MHA_ERR_ALIAS, "mha_sdpa: O overlaps an input");
+
+  mha::SdpaArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.q_sr = d_k, a.q_sh = n_q * d_k, a.q_sb = h * n_q * d_k;
+  a.k_sr = d_k, a.k_sh = n_k * d_k, a.k_sb = h * n_k * d_k;
+  a.v_sr = d_v, a.v_sh = n_k * d_v, a.v_sb = h * n_k * d_v;
+  a.o_sr = d_v, a.o_sh = n_q * d_v, a.o_sb = h * n_q * d_v;
+  a.B = (int32_t)B, a.H = (int32_t)h, a.n_q = (int32_t)n_q, a.n_k = (int32_t)n_k;
+  a.c = std::fabs(scale) * 1.4426950408889634f;
+  a.neg = scale < 0.f ? 1 : 0;
+  a.lens = seq_lens;
+  if (trace_on()) {
+    const double vis = mask_kind == MHA_MASK_CAUSAL ? 0.5 * n_q * (n_q + 1) : (double)n_q * n_k;
+    std::fprintf(stderr,
+                 "[libmha] sdpa dtype=%d B=%lld h=%lld n_q=%lld n_k=%lld d=%lld mask=%d lens=%s "
+                 "rows/wg=%d flops(dense-visible)=%.4g bytes=%.4g\n",
+                 (int)dtype, (long long)B, (long long)h, (long long)n_q, (long long)n_k,
+                 (long long)d_k, (int)mask_kind, seq_lens ? "yes" : "no",
+                 mha::sdpa_rows_per_workgroup(dtype), 4.0 * d_k * vis * B * h,
+                 (double)es * B * h * (2 * n_q * d_k + 2 * n_k * d_k));
+  }
+  const hipError_t e = mha::launch_sdpa(a, dtype, mask_kind == MHA_MASK_CAUSAL, (int)d_k, scale,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mha_sdpa launch");
+  return ok();
+}
+
+size_t mha_forward_workspace_size(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model,
+                                  int32_t h, int32_t dtype) {
+  if (B < 0 || n_q < 0 || n_k < 0 || d_model <= 0 || h <= 0 || d_model % h != 0) return 0;
+  if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16) return 0;
+  return ws_layout(B, n_q, n_k, d_model, dtype).total;
+}
+
+int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* Wk,
+                const void* Wv, const void* Wo, void* out, int32_t dtype, int64_t B,
+                int64_t n_q, int64_t n_k, int64_t d_model, int32_t h, int32_t mask_kind,
+                const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16)
+    return fail(MHA_ERR_DTYPE, "mha_forward: dtype %d", (int)dtype);
+  if (mask_kind != MHA_MASK_NONE && mask_kind != MHA_MASK_CAUSAL)
+    return fail(MHA_ERR_INVALID_ARG, "mha_forward: mask_kind %d", (int)mask_kind);
+  if (B < 0 || n_q < 0 || n_k < 0 || d_model <= 0 || h <= 0)
+    return fail(MHA_ERR_SHAPE, "mha_forward: negative or zero size");
+  if (d_model % h != 0)
+    return fail(MHA_ERR_SHAPE, "mha_forward: d_model %lld not divisible by h %d",
+                (long long)d_model, (int)h);
+  if (n_q > kMaxRows || n_k > kMaxRows || B > 65535 || d_model > 65536 ||
+      B * n_q > ((int64_t)1 << 31) - 1 || B * n_k > ((int64_t)1 << 31) - 1)
+    return fail(MHA_ERR_SHAPE, "mha_forward: size beyond the supported range");
+  const bool self = (x_kv == nullptr || x_kv == x_q);
+  if (self && n_k != n_q)
+    return fail(MHA_ERR_SHAPE, "mha_forward: self-attention needs n_k == n_q");
+  if (mask_kind == MHA_MASK_CAUSAL && n_q != n_k)
+    return fail(MHA_ERR_SHAPE, "mha_forward: causal mask needs n_q == n_k");
+  if (dtype == MHA_F32) return fail(MHA_ERR_UNSUPPORTED, "mha_forward: f32 is not implemented");
+  const int64_t d = d_model / h;
+  if (d != 64) return fail(MHA_ERR_UNSUPPORTED, "mha_forward: head dim %lld (needs 64)", (long long)d);
+  if (B == 0 || n_q == 0) return ok();
+  if (!x_q || !Wq || !Wk || !Wv || !Wo || !out)
+    return fail(MHA_ERR_INVALID_ARG, "mha_forward: null tensor pointer");
+  if (!aligned16(x_q) || !aligned16(x_kv) || !aligned16(Wq) || !aligned16(Wk) ||
+      !aligned16(Wv) || !aligned16(Wo) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(kv_lens) & 3) != 0)
+    return fail(MHA_ERR_INVALID_ARG, "mha_forward: tensors must be 16-byte aligned");
+  const size_t es = elem_size(dtype);
+  const WsLayout L = ws_layout(B, n_q, n_k, d_model, dtype);
+  if (workspace && workspace_bytes < L.total)
+    return fail(MHA_ERR_WORKSPACE, "mha_forward: workspace %zu bytes, needs %zu", workspace_bytes,
+                L.total);
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(MHA_ERR_INVALID_ARG, "mha_forward: workspace not 256-byte aligned");
+  const size_t wbytes = (size_t)(d_model * d_model) * es;
+  const Range ro = range_of(out, (size_t)(B * n_q * d_model) * es);
+  if (overlap(ro, range_of(x_q, (size_t)(B * n_q * d_model) * es)) ||
+      (!self && overlap(ro, range_of(x_kv, (size_t)(B * n_k * d_model) * es))) ||
+      overlap(ro, range_of(Wq, wbytes)) || overlap(ro, range_of(Wk, wbytes)) ||
+      overlap(ro, range_of(Wv, wbytes)) || overlap(ro, range_of(Wo, wbytes)) ||
+      (kv_lens && overlap(ro, range_of(kv_lens, (size_t)B * 4))) ||
+      (workspace && overlap(ro, range_of(workspace, L.total))))
+    return fail(MHA_ERR_ALIAS, "mha_forward: out overlaps an input or the workspace");
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  bool owned = false;
+  if (!ws) {
+    const hipError_t e = hipMallocAsync((void**)&ws, L.total, st);
+    if (e != hipSuccess) return hip_fail(e, "mha_forward workspace allocation");
+    owned = true;
+  }
+  const void* xkv = self ? x_q : x_kv;
+  void* q_ws = ws + L.q;
+  void* k_ws = ws + L.k;
+  void* v_ws = ws + L.v;
+  void* c_ws = ws + L.concat;
+
+  // (1) projections, head-split store [B, h, n, d]
+  mha::GemmArgs g{};
+  g.N = (int32_t)d_model;
+  g.K = (int32_t)d_model;
+  auto split = [&](const void* A, const void* W, void* C, int64_t n) {
+    mha::GemmProblem p{};
+    p.A = A, p.W = W, p.C = C;
+    p.lda = d_model, p.ldw = d_model;
+    p.M = (int32_t)(B * n), p.rows_per_b = (int32_t)n, p.head_dim = (int32_t)d;
+    p.c_sb = h * n * d, p.c_st = d, p.c_sh = n * d;
+    return p;
+  };
+  g.nprob = 0;
+  if (n_k > 0) {
+    g.prob[g.nprob++] = split(x_q, Wq, q_ws, n_q);
+    g.prob[g.nprob++] = split(xkv, Wk, k_ws, n_k);
+    g.prob[g.nprob++] = split(xkv, Wv, v_ws, n_k);
+  }
+  hipError_t e = hipSuccess;
+  if (trace_on())
+    std::fprintf(stderr,
+                 "[libmha] forward dtype=%d B=%lld n_q=%lld n_k=%lld d_model=%lld h=%d mask=%d "
+                 "lens=%s self=%d ws=%zu%s\n",
+                 (int)dtype, (long long)B, (long long)n_q, (long long)n_k, (long long)d_model,
+                 (int)h, (int)mask_kind, kv_lens ? "yes" : "no", self ? 1 : 0, L.total,
+                 owned ? " (allocated)" : "");
+  if (g.nprob) e = mha::launch_gemm(g, dtype, st);
+
+  // (2) attention per head; output in the concat layout [B, n_q, h·d]
+  if (e == hipSuccess) {
+    mha::SdpaArgs a{};
+    a.Q = q_ws, a.K = k_ws, a.V = v_ws, a.O = c_ws;
+    a.q_sr = d, a.q_sh = n_q * d, a.q_sb = h * n_q * d;
+    a.k_sr = d, a.k_sh = n_k * d, a.k_sb = h * n_k * d;
+    a.v_sr = d, a.v_sh = n_k * d, a.v_sb = h * n_k * d;
+    a.o_sr = d_model, a.o_sh = d, a.o_sb = n_q * d_model;
+    a.B = (int32_t)B, a.H = h, a.n_q = (int32_t)n_q, a.n_k = (int32_t)n_k;
+    const float scale = 1.0f / std::sqrt((float)d);
+    a.c = scale * 1.4426950408889634f;
+    a.neg = 0;
+    a.lens = kv_lens;
+    e = mha::launch_sdpa(a, dtype, mask_kind == MHA_MASK_CAUSAL, (int)d, scale, st);
+  }
+  // (3) out = concat · Wo
+  if (e == hipSuccess) {
+    mha::GemmArgs o{};
+    o.N = (int32_t)d_model;
+    o.K = (int32_t)d_model;
+    o.nprob = 1;
+    mha::GemmProblem& p = o.prob[0];
+    p.A = c_ws, p.W = Wo, p.C = out;
+    p.lda = d_model, p.ldw = d_model;
+    p.M = (int32_t)(B * n_q), p.rows_per_b = (int32_t)(B * n_q), p.head_dim = (int32_t)d_model;
+    p.c_sb = 0, p.c_st = d_model, p.c_sh = 0;
+    e = mha::launch_gemm(o, dtype, st);
+  }
+  if (owned) {
+    const hipError_t e2 = hipFreeAsync(ws, st);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e != hipSuccess) return hip_fail(e, "mha_forward launch");
+  return ok();
+}
+
+}  // extern "C"
