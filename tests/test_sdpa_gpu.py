@@ -177,8 +177,8 @@ def test_worked_example_fp32():
     without the causal toggle."""
     fn, _ = gpu_sdpa("f32")
     note("worked example f32")
-    pins.pin_worked_example(fn)
-    pins.pin_worked_example_causal(fn)
+    pins.pin_worked_example(fn, sum_atol=1e-6)
+    pins.pin_worked_example_causal(fn, sum_atol=1e-6)
 
 
 def test_worked_example_bf16_vs_oracle():
@@ -218,7 +218,10 @@ def test_saturation_fp32():
 def test_shift_and_linearity_exact_grid():
     """Softmax shift invariance and linearity in V through the bf16 path,
     on inputs whose shifted / combined values are exactly representable in
-    bf16 (multiples of 1/8 and 1/16 of small magnitude)."""
+    bf16 (multiples of 1/8 and 1/16 of small magnitude).  Both sides of the
+    linearity check carry their own final bf16 rounding, so the
+    coefficients are kept small (|α| + |β| < 1) to keep the sum of those
+    roundings well inside the tolerance."""
     rs = np.random.default_rng(77)
     B, h, n, d = 2, 2, 150, 64
     Q = rs.integers(-8, 9, size=(B, h, n, d)) / 32.0
@@ -227,7 +230,7 @@ def test_shift_and_linearity_exact_grid():
     V2 = rs.integers(-8, 9, size=(B, h, n, d)) / 4.0
     u = np.full(d, 4.0)
     fn, rnd = gpu_sdpa("bf16")
-    for arr in (Q, K, K + u, V1, V2, 0.75 * V1 - 2.5 * V2):
+    for arr in (Q, K, K + u, V1, V2, 0.5 * V1 - 0.25 * V2):
         assert np.array_equal(rnd(arr), arr)
     note("shift/linearity bf16")
     for mask in (oracle.MASK_NONE, oracle.MASK_CAUSAL):
@@ -235,8 +238,8 @@ def test_shift_and_linearity_exact_grid():
         Os = fn(Q, K + u, V1, 0.125, mask, None)
         _check(Os, O, "bf16", f"shift invariance mask={mask}")
         O2 = fn(Q, K, V2, 0.125, mask, None)
-        O12 = fn(Q, K, 0.75 * V1 - 2.5 * V2, 0.125, mask, None)
-        _check(O12, 0.75 * O - 2.5 * O2, "bf16", f"linearity mask={mask}")
+        O12 = fn(Q, K, 0.5 * V1 - 0.25 * V2, 0.125, mask, None)
+        _check(O12, 0.5 * O - 0.25 * O2, "bf16", f"linearity mask={mask}")
 
 
 def test_causal_row0_bit_exact_full_size():

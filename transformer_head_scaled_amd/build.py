@@ -34,6 +34,10 @@ def common_flags():
             # packed fp32 VALU ops are avoided on this hardware; the device
             # compiler otherwise forms them from scalar float code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # keep MFMA accumulators in ordinary VGPRs: the softmax rescales
+            # them with VALU ops, which AGPR-resident accumulators would turn
+            # into copy traffic
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
             f"-I{INCLUDE}", f"-I{CSRC}"]
 

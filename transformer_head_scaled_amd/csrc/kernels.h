@@ -7,10 +7,12 @@
 
 namespace mha {
 
-// Key tile (keys per LDS stage) and query blocks of 32 rows per wave of the
-// bf16/fp16 attention kernel.  One workgroup covers 4 * 32 * kSdpaQB rows.
+// Key tile (keys per LDS stage), query blocks of 32 rows per wave and waves
+// per workgroup of the bf16/fp16 attention kernel.  One workgroup covers
+// kSdpaNW * 32 * kSdpaQB query rows.
 constexpr int kSdpaBN = 64;
-constexpr int kSdpaQB = 1;
+constexpr int kSdpaQB = 2;
+constexpr int kSdpaNW = 4;
 
 // Strides are in elements.  Q/K/V/O rows are d contiguous elements.
 struct SdpaArgs {
@@ -24,6 +26,7 @@ struct SdpaArgs {
   int64_t o_sb, o_sh, o_sr;
   int32_t B, H, n_q, n_k;
   float c;              // |scale| * log2(e)   (MFMA path)
+  float thr;            // lazy-rescale slack, raw score units: 8 / c (inf if c == 0)
   int32_t neg;          // scale < 0: the MFMA path negates Q exactly
   const int32_t* lens;  // device int32[B] valid key counts, or null
 };

@@ -149,6 +149,7 @@ int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype
   a.o_sr = d_v, a.o_sh = n_q * d_v, a.o_sb = h * n_q * d_v;
   a.B = (int32_t)B, a.H = (int32_t)h, a.n_q = (int32_t)n_q, a.n_k = (int32_t)n_k;
   a.c = std::fabs(scale) * 1.4426950408889634f;
+  a.thr = a.c > 0.f ? 8.f / a.c : INFINITY;
   a.neg = scale < 0.f ? 1 : 0;
   a.lens = seq_lens;
   if (trace_on()) {
@@ -275,6 +276,7 @@ int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* W
     a.B = (int32_t)B, a.H = h, a.n_q = (int32_t)n_q, a.n_k = (int32_t)n_k;
     const float scale = 1.0f / std::sqrt((float)d);
     a.c = scale * 1.4426950408889634f;
+    a.thr = 8.f / a.c;
     a.neg = 0;
     a.lens = kv_lens;
     e = mha::launch_sdpa(a, dtype, mask_kind == MHA_MASK_CAUSAL, (int)d, scale, st);

@@ -49,16 +49,42 @@ __device__ __forceinline__ int swz16(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-template <int DT, bool CAUSAL, int BN, int QB>
-__global__ __launch_bounds__(256) void sdpa_fwd_kernel(SdpaArgs p) {
-  constexpr int NW = 4;
+template <int N>
+struct RowVec;  // N 16-bit values as one global/LDS word
+template <>
+struct RowVec<2> {
+  typedef uint32_t T;
+  static __device__ __forceinline__ uint32_t get(T v, int dd) { return (v >> (16 * dd)) & 0xFFFFu; }
+};
+template <>
+struct RowVec<4> {
+  typedef u32x2 T;
+  static __device__ __forceinline__ uint32_t get(T v, int dd) {
+    return (v[dd >> 1] >> (16 * (dd & 1))) & 0xFFFFu;
+  }
+};
+template <>
+struct RowVec<8> {
+  typedef u32x4 T;
+  static __device__ __forceinline__ uint32_t get(T v, int dd) {
+    return (v[dd >> 1] >> (16 * (dd & 1))) & 0xFFFFu;
+  }
+};
+
+// One workgroup: NW waves, each owning QB blocks of 32 query rows (BM = 32·QB·NW
+// rows of one (batch, head)); key/value tiles of BN keys, double-buffered in LDS.
+template <int DT, bool CAUSAL, int BN, int QB, int NW>
+__global__ __launch_bounds__(NW * 64) void sdpa_fwd_kernel(SdpaArgs p) {
+  constexpr int NT = NW * 64;
   constexpr int BM = NW * 32 * QB;
   constexpr int KST = D + 8;   // LDS row stride of K (elements): 144 B, conflict-free 16-B reads
   constexpr int VST = BN + 8;  // LDS row stride of Vᵀ
   constexpr int NKB = BN / 32;
-  constexpr int KCH = BN * D / 8 / 256;  // 16-byte K chunks per thread
-  constexpr int VD = BN / 16;            // d values per thread per key row (4 keys per thread)
-  static_assert(KCH >= 1 && (VD == 4 || VD == 8), "tile shape");
+  constexpr int KCH = BN * D / 8 / NT;  // 16-byte K chunks per thread
+  constexpr int VD = BN / (4 * NW);     // d values per thread per key row (4 keys per thread)
+  static_assert(KCH >= 1 && KCH * 8 * NT == BN * D, "K tile shape");
+  static_assert((VD == 2 || VD == 4 || VD == 8) && VD * 4 * NT == BN * D, "V tile shape");
+  typedef typename RowVec<VD>::T vrow_t;
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KST];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VST];
@@ -85,11 +111,14 @@ __global__ __launch_bounds__(256) void sdpa_fwd_kernel(SdpaArgs p) {
   const uint16_t* Vg = (const uint16_t*)p.V + b * p.v_sb + hh * p.v_sh;
   uint16_t* Og = (uint16_t*)p.O + b * p.o_sb + hh * p.o_sh;
 
+  const int wave_q_first = q0 + wave * QB * 32;
+  const int wave_q_last = wave_q_first + QB * 32 - 1;
+
   // ---- Q fragments (B operand), resident for the whole kernel
   u32x4 qf[QB][4];
 #pragma unroll
   for (int qi = 0; qi < QB; ++qi) {
-    const int row = q0 + (wave * QB + qi) * 32 + l32;
+    const int row = wave_q_first + qi * 32 + l32;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -108,10 +137,10 @@ __global__ __launch_bounds__(256) void sdpa_fwd_kernel(SdpaArgs p) {
     l[qi] = 0.f;
   }
   const float c = p.c;
+  const float thr = p.thr;  // lazy-rescale slack in raw score units
 
   // ---- global -> register -> LDS staging of one K/V tile
   u32x4 kreg[KCH];
-  typedef uint32_t vrow_t __attribute__((ext_vector_type(VD / 2)));
   vrow_t vreg[4];
   constexpr int DG = D / VD;  // threads per key group along d
   const int v_dq = tid % DG, v_kg = tid / DG;
@@ -120,7 +149,7 @@ __global__ __launch_bounds__(256) void sdpa_fwd_kernel(SdpaArgs p) {
     const int kb0 = tile * BN;
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
-      const int ch = tid + r * 256;
+      const int ch = tid + r * NT;
       const int key = kb0 + (ch >> 3);
       u32x4 v = {0u, 0u, 0u, 0u};
       if (key < n_eff) v = *(const u32x4*)(Kg + (int64_t)key * p.k_sr + (ch & 7) * 8);
@@ -137,23 +166,17 @@ __global__ __launch_bounds__(256) void sdpa_fwd_kernel(SdpaArgs p) {
   auto swrite = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
-      const int ch = tid + r * 256;
+      const int ch = tid + r * NT;
       *(u32x4*)&Ks[buf][(ch >> 3) * KST + (ch & 7) * 8] = kreg[r];
     }
     const int pos = (v_kg * 4 & ~15) | swz16(v_kg * 4 & 15);
 #pragma unroll
     for (int dd = 0; dd < VD; ++dd) {
-      const int sh = (dd & 1) * 16;
-      const uint32_t e0 = (vreg[0][dd >> 1] >> sh) & 0xFFFFu;
-      const uint32_t e1 = (vreg[1][dd >> 1] >> sh) & 0xFFFFu;
-      const uint32_t e2 = (vreg[2][dd >> 1] >> sh) & 0xFFFFu;
-      const uint32_t e3 = (vreg[3][dd >> 1] >> sh) & 0xFFFFu;
+      const uint32_t e0 = RowVec<VD>::get(vreg[0], dd), e1 = RowVec<VD>::get(vreg[1], dd);
+      const uint32_t e2 = RowVec<VD>::get(vreg[2], dd), e3 = RowVec<VD>::get(vreg[3], dd);
       *(u32x2*)&Vt[buf][(v_dq * VD + dd) * VST + pos] = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
     }
   };
-
-  const int wave_q_first = q0 + wave * QB * 32;
-  const int wave_q_last = wave_q_first + QB * 32 - 1;
 
   if (ntiles > 0) {
     gload(0);
@@ -167,19 +190,18 @@ __global__ __launch_bounds__(256) void sdpa_fwd_kernel(SdpaArgs p) {
     const int kbase = j * BN;
     const bool wave_live = !CAUSAL || kbase <= wave_q_last;
     if (wave_live) {
+      const uint16_t* Kb = &Ks[buf][l32 * KST + hi * 8];
+      const uint16_t* Vb = &Vt[buf][l32 * VST + hi * 8];
       // ---- Sᵀ = K·Qᵀ for BN keys × 32·QB queries
       f32x16 s[QB][NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int qi = 0; qi < QB; ++qi) s[qi][kb] = f32x16{};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          const u32x4 a = *(const u32x4*)&Ks[buf][(kb * 32 + l32) * KST + st * 16 + hi * 8];
+          const u32x4 a = *(const u32x4*)(Kb + kb * 32 * KST + st * 16);
 #pragma unroll
-          for (int qi = 0; qi < QB; ++qi) s[qi][kb] = mfma_32x32x16<DT>(a, qf[qi][st], s[qi][kb]);
+          for (int qi = 0; qi < QB; ++qi)
+            s[qi][kb] = mfma_32x32x16<DT>(a, qf[qi][st], st == 0 ? f32x16{} : s[qi][kb]);
         }
       }
 
@@ -204,9 +226,24 @@ __global__ __launch_bounds__(256) void sdpa_fwd_kernel(SdpaArgs p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qi][kb][i]);
         mx = pair_max(mx);
-        const float m_new = fmaxf(m[qi], mx);
-        const float alpha = (m[qi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m[qi] - m_new) * c);
-        const float mc = (m_new == -INFINITY ? 0.f : m_new) * c;
+        // Lazy rescaling: the running max only moves when a row's new max
+        // exceeds it by more than thr (weights then stay <= 2^8), and then
+        // for the whole wave at once.  Any reference value gives the same
+        // softmax; the rescale keeps O and l consistent with it exactly.
+        const bool need = (m[qi] == -INFINITY) ? (mx != -INFINITY) : (mx > m[qi] + thr);
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+          const float m_new = fmaxf(m[qi], mx);
+          const float alpha =
+              (m[qi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m[qi] - m_new) * c);
+          m[qi] = m_new;
+          l[qi] *= alpha;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            o[qi][0][i] *= alpha;
+            o[qi][1][i] *= alpha;
+          }
+        }
+        const float mc = (m[qi] == -INFINITY ? 0.f : m[qi]) * c;
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -221,13 +258,7 @@ __global__ __launch_bounds__(256) void sdpa_fwd_kernel(SdpaArgs p) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) pk[qi][kb][i] = pack2<DT>(pv[2 * i], pv[2 * i + 1]);
         }
-        l[qi] = l[qi] * alpha + rs;
-        m[qi] = m_new;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          o[qi][0][i] *= alpha;
-          o[qi][1][i] *= alpha;
-        }
+        l[qi] += rs;
       }
 
       // ---- Oᵀ += Vᵀ·Pᵀ
@@ -237,8 +268,7 @@ __global__ __launch_bounds__(256) void sdpa_fwd_kernel(SdpaArgs p) {
         for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
           for (int db = 0; db < 2; ++db) {
-            const u32x4 a =
-                *(const u32x4*)&Vt[buf][(db * 32 + l32) * VST + kb * 32 + t2 * 16 + hi * 8];
+            const u32x4 a = *(const u32x4*)(Vb + db * 32 * VST + kb * 32 + t2 * 16);
 #pragma unroll
             for (int qi = 0; qi < QB; ++qi) {
               const u32x4 bv = {pk[qi][kb][4 * t2 + 0], pk[qi][kb][4 * t2 + 1],
@@ -278,7 +308,11 @@ __global__ __launch_bounds__(256) void sdpa_fwd_kernel(SdpaArgs p) {
 //
 // Plain fp32 attention for small problems and the 1e-5 parity case: one
 // thread per query row, K/V tiles of 32 keys broadcast from LDS, online
-// softmax with expf.  Any head dimension in {16, 32, 64, 128}.
+// softmax.  Any head dimension in {16, 32, 64, 128}.  Inputs, weights and
+// the output accumulator are fp32; the dot products, the running max and
+// the exponent argument are formed in fp64, so the scores carry no fp32
+// summation error even when they are large (an unscaled softmax), and the
+// only fp32 roundings left are expf and the weighted sum of V.
 template <int DH>
 __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, int causal) {
   constexpr int TK = 32;
@@ -303,7 +337,8 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
     q[d] = row < p.n_q ? Qg[(int64_t)row * p.q_sr + d] : 0.f;
     o[d] = 0.f;
   }
-  float m = -INFINITY, l = 0.f;
+  double m = -INFINITY;
+  float l = 0.f;
 
   for (int j = 0; j < ntiles; ++j) {
     __syncthreads();
@@ -318,27 +353,27 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
       *(float4*)&Vs[e * 4] = vv;
     }
     __syncthreads();
-    float s[TK];
-    float mx = -INFINITY;
+    double s[TK];
+    double mx = -INFINITY;
 #pragma unroll
     for (int k = 0; k < TK; ++k) {
-      float acc = 0.f;
+      double acc = 0.0;
 #pragma unroll
-      for (int d = 0; d < DH; ++d) acc = __builtin_fmaf(q[d], Ks[k * DH + d], acc);
+      for (int d = 0; d < DH; ++d) acc = __builtin_fma((double)q[d], (double)Ks[k * DH + d], acc);
       const int key = j * TK + k;
       const bool vis = key < n_eff && (!causal || key <= row);
-      s[k] = vis ? acc * scale : -INFINITY;
-      mx = fmaxf(mx, s[k]);
+      s[k] = vis ? acc * (double)scale : -INFINITY;
+      mx = fmax(mx, s[k]);
     }
-    const float m_new = fmaxf(m, mx);
-    const float alpha = (m == -INFINITY) ? 0.f : expf(m - m_new);
-    const float mu = m_new == -INFINITY ? 0.f : m_new;
+    const double m_new = fmax(m, mx);
+    const float alpha = (m == -INFINITY) ? 0.f : expf((float)(m - m_new));
+    const double mu = m_new == -INFINITY ? 0.0 : m_new;
     l *= alpha;
 #pragma unroll
     for (int d = 0; d < DH; ++d) o[d] *= alpha;
 #pragma unroll
     for (int k = 0; k < TK; ++k) {
-      const float e = s[k] == -INFINITY ? 0.f : expf(s[k] - mu);
+      const float e = s[k] == -INFINITY ? 0.f : expf((float)(s[k] - mu));
       l += e;
 #pragma unroll
       for (int d = 0; d < DH; ++d) o[d] = __builtin_fmaf(e, Vs[k * DH + d], o[d]);
@@ -352,12 +387,13 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
   }
 }
 
-template <int DT, bool CAUSAL, int BN, int QB>
+template <int DT, bool CAUSAL, int BN, int QB, int NW>
 hipError_t launch_mfma(const SdpaArgs& a, hipStream_t st) {
-  constexpr int BM = 4 * 32 * QB;
+  constexpr int BM = NW * 32 * QB;
   const int64_t nqb = (a.n_q + BM - 1) / BM;
   const int64_t grid = nqb * a.B * a.H;
-  hipLaunchKernelGGL((sdpa_fwd_kernel<DT, CAUSAL, BN, QB>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((sdpa_fwd_kernel<DT, CAUSAL, BN, QB, NW>), dim3((unsigned)grid), dim3(NW * 64),
+                     0, st, a);
   return hipGetLastError();
 }
 
@@ -370,7 +406,7 @@ hipError_t launch_f32(const SdpaArgs& a, float scale, int causal, hipStream_t st
 
 }  // namespace
 
-int sdpa_rows_per_workgroup(int dtype) { return dtype == DT_F32 ? 64 : 4 * 32 * kSdpaQB; }
+int sdpa_rows_per_workgroup(int dtype) { return dtype == DT_F32 ? 64 : kSdpaNW * 32 * kSdpaQB; }
 
 hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float scale, hipStream_t st) {
   if (dtype == DT_F32) {
@@ -384,10 +420,10 @@ hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float sc
   }
   if (d != D) return hipErrorInvalidValue;
   if (dtype == DT_BF16)
-    return causal ? launch_mfma<DT_BF16, true, kSdpaBN, kSdpaQB>(a, st)
-                  : launch_mfma<DT_BF16, false, kSdpaBN, kSdpaQB>(a, st);
-  return causal ? launch_mfma<DT_F16, true, kSdpaBN, kSdpaQB>(a, st)
-                : launch_mfma<DT_F16, false, kSdpaBN, kSdpaQB>(a, st);
+    return causal ? launch_mfma<DT_BF16, true, kSdpaBN, kSdpaQB, kSdpaNW>(a, st)
+                  : launch_mfma<DT_BF16, false, kSdpaBN, kSdpaQB, kSdpaNW>(a, st);
+  return causal ? launch_mfma<DT_F16, true, kSdpaBN, kSdpaQB, kSdpaNW>(a, st)
+                : launch_mfma<DT_F16, false, kSdpaBN, kSdpaQB, kSdpaNW>(a, st);
 }
 
 }  // namespace mha
