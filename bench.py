@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = dict(B=4, h=8, n=4096, d=64)
+COPY_BYTES = 512 << 20   # plain device copy used to calibrate the HBM byte counters
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sdpa_fwd_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "transformer_head_scaled_amd", "csrc", "sdpa_fwd.hip")
 
@@ -89,6 +90,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: libmha runs on one GPU only (no multi-GPU path is built); "
@@ -101,6 +104,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+        return 0
     w = WORKLOAD
     B, h, n, d = w["B"], w["h"], w["n"], w["d"]
     ins = synth.sdpa_inputs(5, B, h, n, n, d, dtype="bf16")

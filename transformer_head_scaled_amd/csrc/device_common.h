@@ -19,6 +19,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;  // LDS-qualified, for ds_read_tr
 
 // D(32x32, fp32) += A(32x16) * B(16x32); 8 half-precision values per lane.
 // Operand layout (lane l, element j): A[row l%32][k 8*(l/32)+j],

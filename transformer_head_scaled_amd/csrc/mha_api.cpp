@@ -148,8 +148,11 @@ int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype
   a.v_sr = d_v, a.v_sh = n_k * d_v, a.v_sb = h * n_k * d_v;
   a.o_sr = d_v, a.o_sh = n_q * d_v, a.o_sb = h * n_q * d_v;
   a.B = (int32_t)B, a.H = (int32_t)h, a.n_q = (int32_t)n_q, a.n_k = (int32_t)n_k;
-  a.c = std::fabs(scale) * 1.4426950408889634f;
-  a.thr = a.c > 0.f ? 8.f / a.c : INFINITY;
+  // c is clamped away from 0: for |scale| this small every visible weight
+  // is exp2(~0) = 1 in fp32 (the uniform softmax scale 0 defines), while
+  // masked scores (-inf) still give exactly 0
+  a.c = std::fmax(std::fabs(scale) * 1.4426950408889634f, 1e-30f);
+  a.thr = 8.f / a.c;
   a.neg = scale < 0.f ? 1 : 0;
   a.lens = seq_lens;
   if (trace_on()) {

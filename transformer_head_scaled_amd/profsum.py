@@ -1,0 +1,102 @@
+"""Summarise rocprofv3 CSV output into the short text/JSON kept under profiles/.
+
+    python -m transformer_head_scaled_amd.profsum stats  <kernel_stats.csv> <out.md> "<command>"
+    python -m transformer_head_scaled_amd.profsum traffic <fetch_dir> <write_dir> \
+        <copy_fetch_dir> <copy_write_dir> <out.json> "<commands>"
+
+``stats`` turns a ``--kernel-trace --stats`` kernel_stats.csv into a markdown
+table.  ``traffic`` reads four ``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE,
+for the attention bench and for a plain device copy of known size), scales
+each counter by known-bytes / counter-reading of the copy, and records the
+HBM bytes per attention launch together with a hash of the kernel source the
+counters were taken on (the bench only reports the figure while the source
+is unchanged).
+"""
+
+import csv
+import collections
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SRC = os.path.join(ROOT, "transformer_head_scaled_amd", "csrc", "sdpa_fwd.hip")
+COPY_BYTES = 512 << 20
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_stats(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def stats_md(csv_path, out_md, command):
+    rows = read_stats(csv_path)
+    lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command, "```", "",
+             "| kernel | calls | average µs | min µs | max µs | share % |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| `{}` | {} | {:.2f} | {:.2f} | {:.2f} | {:.2f} |".format(
+            r["Name"], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def counter_means(run_dir, counter):
+    path = None
+    for dp, _, files in os.walk(run_dir):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                path = os.path.join(dp, fn)
+    if path is None:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    agg = collections.defaultdict(list)
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json, commands):
+    f = counter_means(fetch_dir, "FETCH_SIZE")
+    w = counter_means(write_dir, "WRITE_SIZE")
+    cf = counter_means(cfetch_dir, "FETCH_SIZE")
+    cw = counter_means(cwrite_dir, "WRITE_SIZE")
+    copy_name = max(cf, key=lambda k: cf[k])  # the 512 MiB copy dominates
+    fetch_factor = COPY_BYTES / (cf[copy_name] * 1024.0)
+    write_factor = COPY_BYTES / (cw[copy_name] * 1024.0)
+    res = {"kernel_source_sha256_16": kernel_hash(), "copy_kernel": copy_name,
+           "copy_bytes": COPY_BYTES, "fetch_size_kib_per_copy": cf[copy_name],
+           "write_size_kib_per_copy": cw[copy_name], "fetch_factor": fetch_factor,
+           "write_factor": write_factor, "kernels": {}, "commands": commands}
+    for name in f:
+        if "sdpa_fwd" not in name:
+            continue
+        fb = f[name] * 1024.0 * fetch_factor
+        wb = w.get(name, 0.0) * 1024.0 * write_factor
+        res["kernels"][name] = {"fetch_kib": f[name], "write_kib": w.get(name),
+                                "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+        if ", false," in name:
+            res["noncausal_bytes_per_launch"] = fb + wb
+        elif ", true," in name:
+            res["causal_bytes_per_launch"] = fb + wb
+    with open(out_json, "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+    return res
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        stats_md(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "traffic":
+        print(json.dumps(traffic(*sys.argv[2:7], sys.argv[7]), indent=1))
+    else:
+        raise SystemExit(__doc__)
