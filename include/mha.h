@@ -78,8 +78,8 @@ enum {
  *   seq_lens[b] keys (key padding; clamped to [0, n_k]).  Masked K/V rows
  *   are never read, so their contents (NaN included) have no effect.
  * scale: any finite float; the pages use 1/sqrt(d_k).
- * Supported: BF16/F16 with d_k = d_v = 64 (MFMA flash kernel); F32 with
- *   d_k = d_v in {16, 32, 64, 128}.
+ * Supported: BF16/F16 with d_k = d_v = 64 and n_k·64·2 bytes < 2 GiB (MFMA
+ *   flash kernel); F32 with d_k = d_v in {16, 32, 64, 128}.
  * O must not overlap Q, K, V or seq_lens (MHA_ERR_ALIAS).
  */
 int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype, int64_t B,

@@ -7,29 +7,6 @@
 
 namespace mha {
 
-// Key tile (keys per LDS stage), query blocks of 32 rows per wave and waves
-// per workgroup of the bf16/fp16 attention kernel.  One workgroup covers
-// kSdpaNW * 32 * kSdpaQB query rows.
-constexpr int kSdpaBN = 64;
-constexpr int kSdpaQB = 2;
-constexpr int kSdpaNW = 4;
-// Use the ping-pong kernel (512 rows, 32-key tiles, two wave groups that
-// alternate between MFMA and VALU halves) instead.
-#ifndef MHA_SDPA_PINGPONG
-#define MHA_SDPA_PINGPONG 0
-#endif
-constexpr bool kSdpaPingPong = MHA_SDPA_PINGPONG != 0;
-// LDS stages of the K/V tile ring (2 = double buffering) and whether waves
-// raise their issue priority while issuing MFMAs.
-#ifndef MHA_SDPA_STAGES
-#define MHA_SDPA_STAGES 3
-#endif
-#ifndef MHA_SDPA_PRIO
-#define MHA_SDPA_PRIO 1
-#endif
-constexpr int kSdpaStages = MHA_SDPA_STAGES;
-constexpr bool kSdpaPrio = MHA_SDPA_PRIO != 0;
-
 // Strides are in elements.  Q/K/V/O rows are d contiguous elements.
 struct SdpaArgs {
   const void* Q;
@@ -42,7 +19,6 @@ struct SdpaArgs {
   int64_t o_sb, o_sh, o_sr;
   int32_t B, H, n_q, n_k;
   float c;              // max(|scale| * log2(e), 1e-30)   (MFMA path)
-  float thr;            // lazy-rescale slack in raw score units: 8 / c
   int32_t neg;          // scale < 0: the MFMA path negates Q exactly
   const int32_t* lens;  // device int32[B] valid key counts, or null
 };

@@ -57,6 +57,9 @@ bool overlap(Range a, Range b) {
 }
 
 constexpr int64_t kMaxRows = (int64_t)1 << 30;  // rows per sequence (int32 indexing in kernels)
+// The MFMA kernels address one head's K/V through a buffer resource with a
+// 32-bit byte range.
+constexpr int64_t kMaxBufferBytes = ((int64_t)1 << 31) - 1;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -123,6 +126,9 @@ int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype
       return fail(MHA_ERR_UNSUPPORTED, "mha_sdpa: f32 needs d_k == d_v in {16,32,64,128}");
   } else if (d_k != 64 || d_v != 64) {
     return fail(MHA_ERR_UNSUPPORTED, "mha_sdpa: bf16/f16 needs d_k == d_v == 64");
+  } else if (n_k * d_k * 2 > kMaxBufferBytes) {
+    return fail(MHA_ERR_UNSUPPORTED, "mha_sdpa: one head's K/V exceeds 2 GiB (n_k %lld)",
+                (long long)n_k);
   }
   if (B == 0 || h == 0 || n_q == 0) return ok();
   if (!Q || !O || ((!K || !V) && n_k > 0))
@@ -152,7 +158,6 @@ int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype
   // is exp2(~0) = 1 in fp32 (the uniform softmax scale 0 defines), while
   // masked scores (-inf) still give exactly 0
   a.c = std::fmax(std::fabs(scale) * 1.4426950408889634f, 1e-30f);
-  a.thr = 8.f / a.c;
   a.neg = scale < 0.f ? 1 : 0;
   a.lens = seq_lens;
   if (trace_on()) {
@@ -202,6 +207,9 @@ int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* W
   if (dtype == MHA_F32) return fail(MHA_ERR_UNSUPPORTED, "mha_forward: f32 is not implemented");
   const int64_t d = d_model / h;
   if (d != 64) return fail(MHA_ERR_UNSUPPORTED, "mha_forward: head dim %lld (needs 64)", (long long)d);
+  if (n_k * d * 2 > kMaxBufferBytes)
+    return fail(MHA_ERR_UNSUPPORTED, "mha_forward: one head's K/V exceeds 2 GiB (n_k %lld)",
+                (long long)n_k);
   if (B == 0 || n_q == 0) return ok();
   if (!x_q || !Wq || !Wk || !Wv || !Wo || !out)
     return fail(MHA_ERR_INVALID_ARG, "mha_forward: null tensor pointer");
@@ -279,7 +287,6 @@ int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* W
     a.B = (int32_t)B, a.H = h, a.n_q = (int32_t)n_q, a.n_k = (int32_t)n_k;
     const float scale = 1.0f / std::sqrt((float)d);
     a.c = scale * 1.4426950408889634f;
-    a.thr = 8.f / a.c;
     a.neg = 0;
     a.lens = kv_lens;
     e = mha::launch_sdpa(a, dtype, mask_kind == MHA_MASK_CAUSAL, (int)d, scale, st);
