@@ -9,24 +9,30 @@
 // stream through LDS and an online softmax (running max m and sum l per
 // query row, fp32) rescales the fp32 output accumulator.
 //
-// Work decomposition.  One workgroup = 4 waves x 64 query rows (two blocks
-// of 32) of one (batch, head); 64-key K/V tiles pass through a 3-stage LDS
-// ring.  Scores are formed transposed, Sᵀ = K·Qᵀ, with the 32x32x16 MFMA:
-// K is the A operand (rows = keys, read from LDS), Q the B operand
-// (columns = queries, kept in registers for the whole kernel).  In the
-// MFMA result layout every lane then holds 16 scores of ONE query row (its
-// column), the other 16 of that row sitting in lane l^32 -- so a row max
-// needs a single cross-lane exchange (v_permlane32_swap).
+// Work decomposition.  A workgroup is 4 waves (2 with the causal mask) of
+// one (batch, head); each wave owns 64 query rows as two blocks of 32.
+// 64-key K and V tiles pass through a 2-stage LDS ring.  Scores are formed
+// transposed, Sᵀ = K·Qᵀ, with the 32x32x16 MFMA: K is the A operand (rows
+// = keys, read from LDS), Q the B operand (columns = queries, kept in
+// registers for the whole kernel).  In the MFMA result layout every lane
+// then holds 16 scores of ONE query row (its column), the other 16 of that
+// row sitting in lane l^32 -- so a row max needs a single cross-lane
+// exchange (v_permlane32_swap).
 //
 // The output is formed transposed too, Oᵀ = Vᵀ·Pᵀ: P (rounded to the
 // input dtype) is the B operand and comes straight out of the Sᵀ result
 // registers.  Those registers hold, for lane half h, the keys
 // {4h..4h+3, 8+4h..8+4h+3} of each 16-key step rather than 8 consecutive
-// keys; the contraction order is free, so Vᵀ is staged into LDS transposed
-// with the keys of every 16-group permuted the same way (bits 2 and 3 of
-// the key offset swapped) and each lane reads its 8 values with one
-// 16-byte load.  In the Oᵀ result each lane again holds its own query row,
-// so a rescale of a row of O is a plain per-lane multiply.
+// keys; the contraction order is free, so the Vᵀ fragments are read in the
+// same key order.  V stays row-major in LDS and the fragments come from
+// transposing LDS reads (ds_read_b64_tr_b16, 4 keys x 4 d per 16-lane
+// group).  In the Oᵀ result each lane again holds its own query row, so a
+// rescale of a row of O is a plain per-lane multiply.
+//
+// Schedule.  Per tile a wave computes S for block 0, then S for block 1
+// interleaved with the exponentials of block 0, then P0·V interleaved with
+// the exponentials of block 1, then P1·V, so that the matrix cores and the
+// vector ALU of a SIMD work at the same time.
 //
 // Softmax without a per-tile max.  The reference value m of a row only has
 // to keep the weights finite: with weights p = exp2(s·c − m·c) the softmax
@@ -38,13 +44,18 @@
 // The row sums are accumulated from the rounded weights (one dot2 per pair),
 // the same values P·V uses.
 //
-// Loads.  K and V are read with buffer loads whose range ends at the valid
-// key length, so rows past it read as 0 without per-lane branches: whatever
+// Loads.  K and V tiles go from memory straight into LDS (buffer loads with
+// an LDS destination), with 16-byte chunks of each 128-byte row permuted
+// (XOR with a few bits of the key) so that the fragment reads of a 16-lane
+// phase hit all 64 banks once.  The buffer range ends at the valid key
+// length, so rows past it read as 0 without per-lane branches: whatever
 // the memory there holds -- NaN included -- has no effect, matching the
 // reading that a masked key has weight exactly 0.  Causal tiles entirely
 // above the diagonal are never loaded, tiles a whole wave cannot see are
 // skipped by that wave, and only the diagonal and key-length boundary tiles
 // evaluate the per-element mask.
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -55,11 +66,20 @@ namespace {
 
 constexpr int D = 64;  // head dimension d_k = d_v handled by this kernel
 
-// Position of key offset k (0..15) inside a 16-key group of a transposed
-// Vᵀ row: bits 2 and 3 swapped, the order in which the score registers hold
-// the keys (see the top of this file).
-__device__ __forceinline__ int swz16(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+// 16 bytes per lane from a raw buffer (descriptor rsrc, byte offset voff)
+// straight into LDS: lane i writes bytes [lds + 16i, lds + 16i + 16).  Out-of-
+// range offsets read as zero.  Written as inline assembly so that the
+// compiler does not treat every later LDS read as a possible alias of the
+// transfer and wait for it; the caller orders it with explicit waits and
+// barriers instead.  M0 (the LDS base of the transfer) is set here; nothing
+// else in these kernels reads M0, and the compiler treats it as reserved.
+__device__ __forceinline__ void load_lds_b128(u32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory");
 }
 
 // Sum of the two half-precision weights packed in `w` added to acc (fp32).
@@ -74,23 +94,32 @@ __device__ __forceinline__ float dot2_sum(uint32_t w, float acc) {
   }
 }
 
-template <int DT, bool CAUSAL>
-__global__ __launch_bounds__(256) void sdpa_fwd_kernel(SdpaArgs p) {
-  constexpr int NW = 4, QB = 2, BN = 64, NSTAGE = 3;
-  constexpr int BM = NW * 32 * QB;  // 256 query rows
-  constexpr int KST = D + 8;        // K tile: [key][KST], 144-byte rows
-  constexpr int VST = BN + 8;       // Vᵀ tile: [d][VST], 144-byte rows, permuted keys
+// NW waves per workgroup, each owning 64 query rows (two blocks of 32).
+template <int DT, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sdpa_fwd_kernel(SdpaArgs p) {
+  constexpr int QB = 2, BN = 64, NSTAGE = 2;
+  constexpr int BM = NW * 32 * QB;  // query rows per workgroup
+  constexpr int CPW = 8 / NW;       // 1 KB pieces of a K (or V) tile loaded per wave
   constexpr float kAccept = 256.f;  // accept a tile while partial row sums are <= 2^8
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[NSTAGE][BN * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[NSTAGE][D * VST];
+  // K tile: [key][64], 128-byte rows whose eight 16-byte chunks are
+  // permuted per row (chunk c of key k sits at c ^ ((k >> 1) & 7)), so the
+  // 16 lanes of a fragment read hit 16 different bank groups
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NSTAGE][BN * D];
+  // V tile: [key][64], 128-byte rows, chunk c of key k at c ^ (4 · bit 1 of
+  // k), which keeps the transposing fragment reads conflict-free
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NSTAGE][BN * D];
 
   const int nqb = (p.n_q + BM - 1) / BM;
   const uint32_t total = (uint32_t)nqb * p.B * p.H;
   const uint32_t t = xcd_remap(blockIdx.x, total);
   const int bh = t / nqb;
   int qb = t % nqb;
-  if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
+  // Causal: the work of row block qb grows with qb.  Neighbouring heads
+  // walk their row blocks in opposite directions, so that the workgroups a
+  // compute unit receives (every 32nd of its XCD when they are dealt out
+  // in order) pair long row blocks with short ones.
+  if (CAUSAL && !(bh & 1)) qb = nqb - 1 - qb;
   const int b = bh / p.H, hh = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -109,10 +138,13 @@ __global__ __launch_bounds__(256) void sdpa_fwd_kernel(SdpaArgs p) {
   const uint16_t* Vg = (const uint16_t*)p.V + b * p.v_sb + hh * p.v_sh;
   uint16_t* Og = (uint16_t*)p.O + b * p.o_sb + hh * p.o_sh;
   // buffer resources covering exactly the valid keys of this (batch, head)
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, (int)((int64_t)n_eff * p.k_sr * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)Vg, 0, (int)((int64_t)n_eff * p.v_sr * 2), 0x00020000);
+  // (raw descriptor words: base, stride 0, byte range, format word)
+  const uint64_t kaddr = (uint64_t)(uintptr_t)Kg;
+  const u32x4 krs = {(uint32_t)kaddr, (uint32_t)(kaddr >> 32) & 0xffffu,
+                     (uint32_t)((int64_t)n_eff * p.k_sr * 2), 0x00020000u};
+  const uint64_t vaddr = (uint64_t)(uintptr_t)Vg;
+  const u32x4 vrs = {(uint32_t)vaddr, (uint32_t)(vaddr >> 32) & 0xffffu,
+                     (uint32_t)((int64_t)n_eff * p.v_sr * 2), 0x00020000u};
 
   // ---- Q fragments (B operand), resident for the whole kernel
   u32x4 qf[QB][4];
@@ -139,164 +171,268 @@ __global__ __launch_bounds__(256) void sdpa_fwd_kernel(SdpaArgs p) {
   }
   const float c = p.c;
 
-  // ---- staging: K as is (two 16-byte chunks per thread), V transposed
-  // (4 keys x 4 d per thread, written as four 8-byte runs along the keys)
-  u32x4 kreg[2];
-  u32x2 vreg[4];
-  const int v_dq = tid & 15, v_kg = tid >> 4;
-  const uint32_t k_off0 = (uint32_t)(((tid >> 3) * p.k_sr + (tid & 7) * 8) * 2);
-  const uint32_t k_off1 = (uint32_t)((((tid + 256) >> 3) * p.k_sr + (tid & 7) * 8) * 2);
-  const uint32_t v_off = (uint32_t)(((v_kg * 4) * p.v_sr + v_dq * 4) * 2);
+  // ---- staging.  K and V go straight from memory into LDS (buffer loads
+  // with an LDS destination: each wave instruction fills 1 KB = 8 keys, lane
+  // i writing bytes [16i, 16i + 16)); every lane fetches the 16-byte chunk
+  // that the permuted layout puts at its position.
+  uint32_t k_off[CPW], v_off[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int q = (wave * CPW + i) * 64 + lane;  // LDS chunk this lane fills
+    const int key = q >> 3;
+    k_off[i] = (uint32_t)((key * p.k_sr + ((q & 7) ^ ((key >> 1) & 7)) * 8) * 2);
+    v_off[i] = (uint32_t)((key * p.v_sr + ((q & 7) ^ (((key >> 1) & 1) << 2)) * 8) * 2);
+  }
   const uint32_t k_tile = (uint32_t)(BN * p.k_sr * 2), v_tile = (uint32_t)(BN * p.v_sr * 2);
-  const uint32_t v_row = (uint32_t)(p.v_sr * 2);
 
-  auto gload = [&](int tile) {
-    kreg[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_off0 + tile * k_tile, 0, 0));
-    kreg[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_off1 + tile * k_tile, 0, 0));
+  // issue this wave's two LDS-destination loads of K (or V) for one tile.
+  // The K and V halves are issued at different points of a step, so that
+  // the waves of a compute unit do not all queue their loads at once.
+  auto gload_k = [&](int tile, int stage) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      vreg[r] = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, v_off + tile * v_tile + r * v_row, 0, 0));
+    for (int i = 0; i < CPW; ++i)
+      // (the destinations are per wave: readfirstlane makes them scalars)
+      load_lds_b128(krs,
+                    __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+                        __attribute__((address_space(3))) void*)&Ks[stage][(wave * CPW + i) * 512]),
+                    k_off[i] + tile * k_tile);
   };
-  auto swrite = [&](int stage) {
-    *(u32x4*)&Ks[stage][(tid >> 3) * KST + (tid & 7) * 8] = kreg[0];
-    *(u32x4*)&Ks[stage][((tid + 256) >> 3) * KST + (tid & 7) * 8] = kreg[1];
-    const int pos = (v_kg * 4 & ~15) | swz16(v_kg * 4 & 15);
-    uint16_t* vt = &Vt[stage][(v_dq * 4) * VST + pos];
+  auto gload_v = [&](int tile, int stage) {
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      // d = 4·v_dq + 2·h2 (low halves) and + 1 (high halves)
-      const uint32_t lo01 = __builtin_amdgcn_perm(vreg[1][h2], vreg[0][h2], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(vreg[3][h2], vreg[2][h2], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(vreg[1][h2], vreg[0][h2], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(vreg[3][h2], vreg[2][h2], 0x07060302u);
-      *(u32x2*)(vt + (2 * h2) * VST) = u32x2{lo01, lo23};
-      *(u32x2*)(vt + (2 * h2 + 1) * VST) = u32x2{hi01, hi23};
+    for (int i = 0; i < CPW; ++i)
+      load_lds_b128(vrs,
+                    __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+                        __attribute__((address_space(3))) void*)&Vs[stage][(wave * CPW + i) * 512]),
+                    v_off[i] + tile * v_tile);
+  };
+  // K fragment (kb, st) of this lane: key kb·32 + l32, chunk 2·st + hi
+  const int kx = (l32 >> 1) & 7;
+  auto kfrag = [&](int buf, int kb, int st) {
+    return *(const u32x4*)&Ks[buf][(kb * 32 + l32) * D + (((2 * st + hi) ^ kx) * 8)];
+  };
+  // Vᵀ fragment (kb, t2, db): d = db·32 + l32 and the 8 keys that the score
+  // registers hold for this lane half, {4·hi .. 4·hi+3, 8+4·hi .. 8+4·hi+3}
+  // of 16-key step kb·32 + t2·16.  Two transposing reads, 4 keys each: lane
+  // i of a 16-lane group points at key (i / 4) of the 4 and at d columns
+  // 4·(i % 4) .. +3 of its 16; the read hands lane r element r % 4 of lane
+  // 4j + r / 4, i.e. key j at column r.
+  const int i16 = lane & 15;
+  const int v_key_l = 4 * hi + (i16 >> 2);          // key offset within a 16-key step (+ 8·e)
+  const int v_x = ((v_key_l >> 1) & 1) << 2;         // the row permutation (bit 1 of the key)
+  const int v_col = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);  // d within the 32-column block
+  auto vfrag = [&](int buf, int kb, int t2, int db) {
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int key = kb * 32 + t2 * 16 + 8 * e + v_key_l;
+      const int d = db * 32 + v_col;
+      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)&Vs[buf][key * D + (((d >> 3) ^ v_x) * 8) + (d & 7)]);
+      const u32x2 w = __builtin_bit_cast(u32x2, v);
+      r[2 * e] = w[0];
+      r[2 * e + 1] = w[1];
     }
+    return r;
   };
 
 #pragma unroll
   for (int t0 = 0; t0 < NSTAGE - 1; ++t0)
     if (t0 < ntiles) {
-      gload(t0);
-      swrite(t0);
+      gload_k(t0, t0);
+      gload_v(t0, t0);
     }
-  __syncthreads();
+  // tile 0 has landed (at most the four loads of tile 1 are outstanding),
+  // then the workgroup barrier; the "memory" clobber keeps LDS accesses on
+  // their side of it
+  if (NSTAGE > 2 && ntiles > 1)
+    __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
 
-  for (int j = 0; j < ntiles; ++j) {
+  // weights of key block kb of query block qi against the current reference
+  // value; returns their partial row sum
+  auto weights = [&](int qi, int kb, const f32x16& sv, uint32_t (&pw)[8]) {
+    float rs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], c, -mc[qi]));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], c, -mc[qi]));
+      pw[i] = pack2<DT>(e0, e1);
+      rs = dot2_sum<DT>(pw[i], rs);
+    }
+    return rs;
+  };
+  // per-element mask of query block qi (diagonal and key-length boundary
+  // tiles only)
+  auto apply_mask = [&](int qi, int kbase, int kb, f32x16& sv) {
+    const int row = wave_q_first + qi * 32 + l32;
+    // visible iff the register's key offset in the tile (a constant) < lim
+    int lim = (CAUSAL ? min(n_eff, row + 1) : n_eff) - kbase - 4 * hi;
+    // opaque to the optimiser: otherwise it hoists one loop-invariant
+    // threshold per register out of the key loop (32 extra registers)
+    asm volatile("" : "+v"(lim));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int off = kb * 32 + 8 * (i >> 2) + (i & 3);
+      sv[i] = off < lim ? sv[i] : -INFINITY;
+    }
+  };
+  // Sᵀ of query block qi, key block kb, for the keys of LDS stage buf,
+  // masked like the tile
+  auto scores = [&](auto masked, int qi, int buf, int kbase, int kb) {
+    f32x16 sv = {};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) sv = mfma_32x32x16<DT>(kfrag(buf, kb, st), qf[qi][st], sv);
+    if constexpr (decltype(masked)::value) apply_mask(qi, kbase, kb, sv);
+    return sv;
+  };
+  // accept the tile's weights of query block qi, or take the exact path:
+  // row max, new reference value, rescale of O and l, weights again.  The
+  // exact path recomputes the scores from LDS (twice, one key block at a
+  // time) instead of keeping them, which keeps the common path's register
+  // footprint small.
+  auto settle = [&](auto masked, int qi, int buf, int kbase, uint32_t (&pw)[2][8], float rs) {
+    // `!(rs <= kAccept)` is also true for NaN
+    const bool reject = (m[qi] == -INFINITY) || !(rs <= kAccept);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(reject) != 0, 0)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const f32x16 sv = scores(masked, qi, buf, kbase, kb);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+      }
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m[qi], mx);
+      const float alpha = (m[qi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m[qi] - m_new) * c);
+      m[qi] = m_new;
+      mc[qi] = (m_new == -INFINITY ? 0.f : m_new) * c;
+      l[qi] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        o[qi][0][i] *= alpha;
+        o[qi][1][i] *= alpha;
+      }
+      rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) rs += weights(qi, kb, scores(masked, qi, buf, kbase, kb), pw[kb]);
+    }
+    l[qi] += rs;
+  };
+
+  // One 64-key tile for this wave's two query blocks.  The instruction
+  // order lets one block's exponentials issue between the matrix
+  // instructions of the other:
+  //   S0 (MFMA), then S1 (MFMA) interleaved with the weights of block 0,
+  //   P0·V (MFMA) interleaved with the weights of block 1, then P1·V.
+  auto tile = [&](auto masked, int buf, int kbase, auto&& mid) {
+    constexpr bool MASKED = decltype(masked)::value;
+    u32x4 kf[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) kf[kb][st] = kfrag(buf, kb, st);
+    f32x16 s0[2], s1[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        s0[kb] = mfma_32x32x16<DT>(kf[kb][st], qf[0][st], st == 0 ? f32x16{} : s0[kb]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        s1[kb] = mfma_32x32x16<DT>(kf[kb][st], qf[1][st], st == 0 ? f32x16{} : s1[kb]);
+    if constexpr (MASKED) {
+      apply_mask(0, kbase, 0, s0[0]);
+      apply_mask(0, kbase, 1, s0[1]);
+    }
+    uint32_t p0[2][8], p1[2][8];
+    const float rs0 = weights(0, 0, s0[0], p0[0]) + weights(0, 1, s0[1], p0[1]);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);  // then VALU / transcendental
+    }
+    u32x4 vf[2][2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+          vf[kb][t2][db] = vfrag(buf, kb, t2, db);
+    settle(masked, 0, buf, kbase, p0, rs0);
+    mid();
+
+
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const u32x4 bv = {p0[kb][4 * t2], p0[kb][4 * t2 + 1], p0[kb][4 * t2 + 2], p0[kb][4 * t2 + 3]};
+          o[0][db] = mfma_32x32x16<DT>(vf[kb][t2][db], bv, o[0][db]);
+        }
+    if constexpr (MASKED) {
+      apply_mask(1, kbase, 0, s1[0]);
+      apply_mask(1, kbase, 1, s1[1]);
+    }
+    const float rs1 = weights(1, 0, s1[0], p1[0]) + weights(1, 1, s1[1], p1[1]);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);
+    }
+    settle(masked, 1, buf, kbase, p1, rs1);
+
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const u32x4 bv = {p1[kb][4 * t2], p1[kb][4 * t2 + 1], p1[kb][4 * t2 + 2], p1[kb][4 * t2 + 3]};
+          o[1][db] = mfma_32x32x16<DT>(vf[kb][t2][db], bv, o[1][db]);
+        }
+  };
+
+  // One step of the key loop: start the loads of tile j + NSTAGE - 1,
+  // compute tile j, barrier.
+  auto step = [&](int j, auto masked) {
     const int buf = j % NSTAGE;
-    if (j + NSTAGE - 1 < ntiles) gload(j + NSTAGE - 1);
+    const bool more = j + NSTAGE - 1 < ntiles;
+    if (more) gload_k(j + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE);
+    auto load_v = [&]() {
+      if (more) gload_v(j + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE);
+    };
     const int kbase = j * BN;
-    const bool wave_live = !CAUSAL || kbase <= wave_q_last;
-    if (wave_live) {
-      const uint16_t* Kb = &Ks[buf][l32 * KST + hi * 8];
-      const uint16_t* Vb = &Vt[buf][l32 * VST + hi * 8];
-      // ---- Sᵀ = K·Qᵀ for 64 keys × 64 queries
-      __builtin_amdgcn_s_setprio(1);
-      f32x16 s[QB][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const u32x4 a = *(const u32x4*)(Kb + kb * 32 * KST + st * 16);
-#pragma unroll
-          for (int qi = 0; qi < QB; ++qi)
-            s[qi][kb] = mfma_32x32x16<DT>(a, qf[qi][st], st == 0 ? f32x16{} : s[qi][kb]);
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-
-      // only the diagonal tile (causal) and the key-length boundary tile
-      // need the per-element mask
-      const bool need_mask = (kbase + BN > n_eff) || (CAUSAL && kbase + BN - 1 > wave_q_first);
-      if (need_mask) {
-        // an opaque statement keeps the compiler from turning this uniform
-        // branch into per-element selects on every tile
-        asm volatile("");
-#pragma unroll
-        for (int qi = 0; qi < QB; ++qi) {
-          const int row = wave_q_first + qi * 32 + l32;
-          // visible iff the register's key offset in the tile (a constant) < lim
-          const int lim = (CAUSAL ? min(n_eff, row + 1) : n_eff) - kbase - 4 * hi;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int off = kb * 32 + 8 * (i >> 2) + (i & 3);
-              s[qi][kb][i] = off < lim ? s[qi][kb][i] : -INFINITY;
-            }
-        }
-      }
-
-      uint32_t pk[QB][2][8];  // P rounded to the input dtype, packed in pairs
-#pragma unroll
-      for (int qi = 0; qi < QB; ++qi) {
-        // weights against the current reference value
-        auto weights = [&]() {
-          float rs = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qi][kb][2 * i], c, -mc[qi]));
-              const float e1 =
-                  __builtin_amdgcn_exp2f(__builtin_fmaf(s[qi][kb][2 * i + 1], c, -mc[qi]));
-              pk[qi][kb][i] = pack2<DT>(e0, e1);
-              rs = dot2_sum<DT>(pk[qi][kb][i], rs);
-            }
-          return rs;
-        };
-        float rs = weights();
-        // accept unless a weight may exceed 2^8 (or is not finite), or the
-        // row has no reference value yet; `!(rs <= kAccept)` is also true
-        // for NaN
-        const bool reject = (m[qi] == -INFINITY) || !(rs <= kAccept);
-        if (__builtin_expect(__builtin_amdgcn_ballot_w64(reject) != 0, 0)) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qi][kb][i]);
-          mx = pair_max(mx);
-          const float m_new = fmaxf(m[qi], mx);
-          const float alpha =
-              (m[qi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m[qi] - m_new) * c);
-          m[qi] = m_new;
-          mc[qi] = (m_new == -INFINITY ? 0.f : m_new) * c;
-          l[qi] *= alpha;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            o[qi][0][i] *= alpha;
-            o[qi][1][i] *= alpha;
-          }
-          rs = weights();
-        }
-        l[qi] += rs;
-      }
-
-      // ---- Oᵀ += Vᵀ·Pᵀ
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-#pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            const u32x4 a = *(const u32x4*)(Vb + db * 32 * VST + kb * 32 + t2 * 16);
-#pragma unroll
-            for (int qi = 0; qi < QB; ++qi) {
-              const u32x4 bv = {pk[qi][kb][4 * t2 + 0], pk[qi][kb][4 * t2 + 1],
-                                pk[qi][kb][4 * t2 + 2], pk[qi][kb][4 * t2 + 3]};
-              o[qi][db] = mfma_32x32x16<DT>(a, bv, o[qi][db]);
-            }
-          }
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-    }
-    if (j + NSTAGE - 1 < ntiles) swrite((j + NSTAGE - 1) % NSTAGE);
-    __syncthreads();
-  }
+    // causal: tiles wholly above this wave's rows are skipped
+    if (!decltype(masked)::value || !CAUSAL || kbase <= wave_q_last)
+      tile(masked, buf, kbase, load_v);
+    else
+      load_v();
+    // Before the barrier, this wave's loads of tile j + 1 have landed: only
+    // the four issued in this step may still be outstanding (none if it
+    // issued none, or with two stages, where tile j + 1 is this step's).
+    if (NSTAGE > 2 && more)
+      __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+  };
+  // Tiles before jd need no per-element mask: they lie below this wave's
+  // diagonal (causal) and inside the valid keys.  Two loops, so that each
+  // holds one variant of the tile code.  Every wave still takes part in
+  // all ntiles barriers.
+  int jd = min(n_eff / BN, ntiles);
+  if (CAUSAL) jd = min(jd, wave_q_first / BN);
+  int j = 0;
+  for (; j < jd; ++j) step(j, std::false_type{});
+  for (; j < ntiles; ++j) step(j, std::true_type{});
 
   // ---- normalise and store this lane's query row (4 consecutive d per store)
 #pragma unroll
@@ -402,11 +538,21 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
   }
 }
 
+// Workgroup size: 4 waves (256 rows) without the causal mask.  With it the
+// work of a row block grows with its index; 2 waves (128 rows) give twice
+// as many workgroups as fit at once, dispatched longest first, so the
+// hardware can even out the compute units.
+template <bool CAUSAL>
+constexpr int waves_per_wg() {
+  return CAUSAL ? 2 : 4;
+}
+
 template <int DT, bool CAUSAL>
 hipError_t launch_mfma(const SdpaArgs& a, hipStream_t st) {
-  const int64_t nqb = (a.n_q + 255) / 256;
+  constexpr int NW = waves_per_wg<CAUSAL>();
+  const int64_t nqb = (a.n_q + NW * 64 - 1) / (NW * 64);
   const int64_t grid = nqb * a.B * a.H;
-  hipLaunchKernelGGL((sdpa_fwd_kernel<DT, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((sdpa_fwd_kernel<DT, CAUSAL, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -419,7 +565,9 @@ hipError_t launch_f32(const SdpaArgs& a, float scale, int causal, hipStream_t st
 
 }  // namespace
 
-int sdpa_rows_per_workgroup(int dtype) { return dtype == DT_F32 ? 64 : 256; }
+int sdpa_rows_per_workgroup(int dtype, int causal) {
+  return dtype == DT_F32 ? 64 : (causal ? waves_per_wg<true>() : waves_per_wg<false>()) * 64;
+}
 
 hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float scale, hipStream_t st) {
   if (dtype == DT_F32) {
