@@ -54,6 +54,107 @@ def measured_traffic():
     return t.get("noncausal_bytes_per_launch")
 
 
+def mha_flops(B, n_q, n_k, d_model, h, causal=False, lens=None):
+    """Algorithmic flops of mha_forward: four projections (2·M·N·K each) plus
+    4·d per visible (query, key) pair."""
+    d = d_model // h
+    proj = 2.0 * d_model * d_model * (2 * B * n_q + 2 * B * n_k)
+    if lens is not None:
+        pairs = float(n_q) * float(sum(int(x) for x in lens))
+    elif causal:
+        pairs = B * n_q * (n_q + 1) / 2.0
+    else:
+        pairs = float(B) * n_q * n_k
+    return proj + 4.0 * d * pairs * h
+
+
+def time_calls(fn, stream, iters, flush=None):
+    """Per-call device time (µs) of fn() with HIP events on ``stream``.  With
+    ``flush`` (a callable that overwrites a large buffer) every call starts
+    with cold caches.  Returns (median, min)."""
+    import numpy as np
+    import torch
+    ts = []
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ts])
+    return float(np.median(us)), float(us.min())
+
+
+def other_configs(dev, stream, iters=100):
+    """The other workloads of the hot path, timed warm (and cold where the
+    working set fits the 256 MB last-level cache): mha_forward self
+    attention with key padding (B 32, n 64, d_model 512, h 8), causal SDPA
+    (B 16, h 8, n 512), mha_forward cross attention (B 8, n_q 384, n_k 512,
+    d_model 1024, h 16).  Rates use algorithmic flops and bytes."""
+    import numpy as np
+    import torch
+    from transformer_head_scaled_amd import libmha, synth
+
+    def dev_t(st):
+        return torch.from_numpy(np.ascontiguousarray(st).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flush():
+        scratch.fill_(1)
+
+    res = {}
+    for cfg in (2, 4):
+        w = synth.WORKLOADS[cfg]
+        ins, lens = synth.workload_inputs(cfg)
+        t = {k: dev_t(v[0]) for k, v in ins.items()}
+        lens_d = None if lens is None else torch.from_numpy(lens).to(dev)
+        B, n_q, n_k, dm, h = w["B"], w["n_q"], w["n_k"], w["d_model"], w["h"]
+        ws = torch.empty(libmha.workspace_size(B, n_q, n_k, dm, h, 1), dtype=torch.uint8, device=dev)
+        out = torch.empty((B, n_q, dm), dtype=torch.bfloat16, device=dev)
+
+        def call():
+            libmha.forward(t["x_q"], t["Wq"], t["Wk"], t["Wv"], t["Wo"], h, x_kv=t.get("x_kv"),
+                           kv_lens=lens_d, out=out, workspace=ws, stream=stream)
+        for _ in range(20):
+            call()
+        med, mn = time_calls(call, stream, iters)
+        fl = mha_flops(B, n_q, n_k, dm, h, lens=lens)
+        nbytes = 2 * (B * n_q * dm * 2 + (B * n_k * dm if w["cross"] else 0) + 4 * dm * dm)
+        entry = {"call": "mha_forward", "us_median": round(med, 2), "us_min": round(mn, 2),
+                 "tflops": round(fl / (med * 1e-6) / 1e12, 2), "flops": fl, "bytes": nbytes}
+        if cfg == 2:
+            cmed, cmn = time_calls(call, stream, max(iters // 4, 10), flush)
+            entry["us_median_cold"] = round(cmed, 2)
+        res[w["name"]] = entry
+    w = synth.WORKLOADS[3]
+    ins, _ = synth.workload_inputs(3)
+    Q, K, V = (dev_t(ins[k][0]) for k in "QKV")
+    O = torch.empty_like(Q)
+
+    def call3():
+        libmha.sdpa(Q, K, V, scale=0.125, mask="causal", out=O, stream=stream)
+    for _ in range(20):
+        call3()
+    med, mn = time_calls(call3, stream, iters)
+    cmed, _ = time_calls(call3, stream, max(iters // 4, 10), flush)
+    fl = sdpa_flops(w["B"], w["h"], w["n_q"], w["n_k"], w["d"], True)
+    nbytes = 4 * w["B"] * w["h"] * w["n_q"] * w["d"] * 2
+    res[w["name"]] = {"call": "mha_sdpa causal", "us_median": round(med, 2), "us_min": round(mn, 2),
+                      "us_median_cold": round(cmed, 2),
+                      "tflops": round(fl / (med * 1e-6) / 1e12, 2),
+                      "gbs": round(nbytes / (med * 1e-6) / 1e9, 1),
+                      "gbs_cold": round(nbytes / (cmed * 1e-6) / 1e9, 1),
+                      "hbm_frac_cold": round(nbytes / (cmed * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                      "flops": fl, "bytes": nbytes}
+    del scratch
+    return res
+
+
 def cpu_baseline(ins, budget_s=12.0):
     """The fp64 oracle, untuned, on a bounded sample of the same workload:
     whole (batch, head) pairs, alternating unmasked and causal, until the
@@ -93,6 +194,8 @@ def main():
                     help="untimed steps before the warmup until this much time has passed, so that "
                          "the GPU clocks have ramped up when timing starts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the timings of the smaller workloads (reported under other_configs)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (for scaling HBM counters)")
@@ -211,6 +314,8 @@ def main():
                             "unit": "TFLOP/s", "frac": round(ach_c / PEAK_BF16_TFLOPS, 4),
                             "kernel": "sdpa_fwd_kernel<bf16, causal, 2 waves>"},
     }
+    if not args.no_other_configs:
+        res["other_configs"] = other_configs(dev, stream)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(ins, args.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -74,6 +74,30 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// 16 bytes per lane from a raw buffer (descriptor rsrc, byte offset voff)
+// straight into LDS: lane i writes bytes [lds + 16i, lds + 16i + 16).  Out-of-
+// range offsets read as zero.  Written as inline assembly so that the
+// compiler does not treat every later LDS read as a possible alias of the
+// transfer and wait for it; the caller orders it with explicit waits and
+// barriers instead.  M0 (the LDS base of the transfer) is set here; nothing
+// else in these kernels reads M0, and the compiler treats it as reserved.
+__device__ __forceinline__ void load_lds_b128(u32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+// Raw buffer descriptor words for `base` with a range of `bytes` bytes
+// (stride 0, the data format word the gfx950 raw buffer loads use).  Loads
+// at offsets >= bytes return zero.
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
 // Map the hardware workgroup index onto a logical tile index so that
 // consecutive logical tiles run on the same XCD (workgroups are dealt to
 // the 8 XCDs round-robin; each XCD has its own L2).

@@ -10,11 +10,18 @@
 // C = A·W with A [M, K] (K contiguous) and W [K, N] (N contiguous), bf16 or
 // fp16 in, fp32 accumulate, rounded once (RNE) on store.  The MFMA needs 8
 // consecutive k per lane in both operands, so the kernel computes
-// Cᵀ = Wᵀ·Aᵀ: A tiles are staged to LDS as they are, W tiles are transposed
-// while being staged (four k-rows per thread, written as 8-byte runs along
-// k).  In the Cᵀ result layout a lane holds 4 consecutive n of one row m,
-// written as one 8-byte store, and the head split / concat is folded into
-// the store address (see GemmProblem).
+// Cᵀ = Wᵀ·Aᵀ with the 32x32x16 MFMA: the B operand (Aᵀ) is a 16-byte read
+// of an A row, the A operand (Wᵀ) comes from transposing LDS reads
+// (ds_read_b64_tr_b16) of the row-major W tile.  In the Cᵀ result a lane
+// holds 4 consecutive n of one row m, written as one 8-byte store, and the
+// head split / concat is folded into the store address (see GemmProblem).
+//
+// Tiles: TM × TN outputs per workgroup of 4 waves (2 × 2, each TM/2 × TN/2),
+// 64 k per stage, two LDS stages.  A and W tiles go from memory straight
+// into LDS (buffer loads with an LDS destination; the buffer range ends at
+// row M of A, so rows past it read as zero).  LDS rows are stored with
+// their 16-byte chunks XOR-permuted by row bits so that every fragment read
+// phase touches each bank once.
 //
 // Up to three independent problems (the Q, K and V projections) share one
 // launch: blockIdx.y selects the problem.
@@ -26,70 +33,118 @@ namespace mha {
 
 namespace {
 
-constexpr int BK = 32;       // k per LDS stage (two 16-k MFMA steps)
-constexpr int AST = BK + 8;  // LDS row stride (elements) of both tiles: 80 B
+constexpr int BK = 64;  // k per LDS stage (four 16-k MFMA steps); A rows are 128 bytes
 
-template <int DT, int TM, int TN>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-  constexpr int WM = TM / 64;  // 32-row m blocks per wave (waves tiled 2 x 2)
-  constexpr int WN = TN / 64;  // 32-col n blocks per wave
-  constexpr int ACH = TM * BK / 8 / 256;  // 16-byte A chunks per thread
-  constexpr int VN = TN / 32;             // n values per thread per k row (4 k rows per thread)
-  static_assert(ACH >= 1 && (VN == 2 || VN == 4), "tile shape");
+#ifndef GEMM_STAGES_128
+#define GEMM_STAGES_128 2
+#endif
+#ifndef GEMM_STAGES_64
+#define GEMM_STAGES_64 2
+#endif
+#ifndef GEMM_HUGE
+#define GEMM_HUGE 0
+#endif
+#ifndef GEMM_BIG_MIN
+#define GEMM_BIG_MIN 256   // 128 x 128 tiles once there are enough to give each CU one
+#endif
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][TM * AST];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][TN * AST];
+// TM x TN outputs per workgroup; each wave computes WTM x WTN of them.
+template <int DT, int TM, int TN, int WTM, int WTN, int NSTAGE>
+__global__ __launch_bounds__((TM / WTM) * (TN / WTN) * 64) void gemm_kernel(GemmArgs g) {
+  constexpr int NWN = TN / WTN;              // waves along n
+  constexpr int NWAVES = (TM / WTM) * NWN;
+  constexpr int WM = WTM / 32;               // 32-row m blocks per wave
+  constexpr int WN = WTN / 32;               // 32-col n blocks per wave
+  constexpr int ACH = TM * 128 / 1024 / NWAVES;     // 1 KB A pieces per wave and stage
+  constexpr int WCH = BK * TN * 2 / 1024 / NWAVES;  // 1 KB W pieces per wave and stage
+  constexpr int WCR = TN / 8;         // 16-byte chunks per W row
+  static_assert(ACH >= 1 && WCH >= 1 && (TN == 64 || TN == 128), "tile shape");
 
-  const GemmProblem& P = g.prob[blockIdx.y];
+  __shared__ __attribute__((aligned(16))) uint16_t As[NSTAGE][TM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[NSTAGE][BK * TN];
+
+  // Workgroups are dealt to the 8 XCDs round-robin (in linear order); the
+  // remap gives each XCD a contiguous run of tiles, i.e. whole row blocks
+  // of A (n is the fastest tile index), which then share that XCD's L2.
+  const uint32_t lin = xcd_remap(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  const GemmProblem& P = g.prob[lin / gridDim.x];
   const int tiles_n = g.N / TN;
   const int tiles_m = (P.M + TM - 1) / TM;
-  const int tile = blockIdx.x;
+  const int tile = lin % gridDim.x;
   if (tile >= tiles_m * tiles_n) return;
   const int tm = tile / tiles_n, tn = tile % tiles_n;
   const int m0 = tm * TM, n0 = tn * TN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5, i16 = lane & 15, g16 = (lane >> 4) & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
 
-  const uint16_t* Ag = (const uint16_t*)P.A;
-  const uint16_t* Wg = (const uint16_t*)P.W;
+  // chunk permutations: A rows (128 bytes) by bits 1..3 of the row; W rows
+  // (128 or 256 bytes) by the row's position among 4 consecutive k, so that
+  // the 4 (or 2 x 4) rows a transposing read touches fall on distinct banks
+  auto a_swz = [](int m) { return (m >> 1) & 7; };
+  auto w_swz = [](int k) { return TN == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); };
 
-  u32x4 areg[ACH];
-  typedef uint32_t wrow_t __attribute__((ext_vector_type(VN / 2)));
-  wrow_t wreg[4];
-  constexpr int NG = TN / VN;  // threads along n
-  const int w_nq = tid % NG, w_kg = tid / NG;  // w_kg in [0, 8): k rows 4*w_kg .. +3
+  // A: descriptor over this workgroup's rows; per lane, the byte offset of
+  // its chunk within a k stage
+  const int a_rows = min(TM, P.M - m0);
+  const u32x4 ars = raw_rsrc((const uint16_t*)P.A + (int64_t)m0 * P.lda,
+                             (uint32_t)((int64_t)a_rows * P.lda * 2));
+  uint32_t a_off[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int q = (wave * ACH + i) * 64 + lane;  // LDS chunk this lane fills
+    const int m = q >> 3;
+    a_off[i] = (uint32_t)(m * P.lda * 2 + ((q & 7) ^ a_swz(m)) * 16);
+  }
+  uint32_t w_off[WCH];
+#pragma unroll
+  for (int i = 0; i < WCH; ++i) {
+    const int q = (wave * WCH + i) * 64 + lane;
+    const int k = q / WCR;
+    w_off[i] = (uint32_t)(k * P.ldw * 2 + ((q % WCR) ^ w_swz(k)) * 16);
+  }
+  const uint16_t* Wg = (const uint16_t*)P.W + n0;
 
-  auto gload = [&](int kt) {
+  auto gload = [&](int kt, int stage) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int r = 0; r < ACH; ++r) {
-      const int ch = tid + r * 256;
-      const int row = m0 + ch / (BK / 8);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < P.M) v = *(const u32x4*)(Ag + (int64_t)row * P.lda + k0 + (ch % (BK / 8)) * 8);
-      areg[r] = v;
-    }
+    for (int i = 0; i < ACH; ++i)
+      load_lds_b128(ars,
+                    __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+                        __attribute__((address_space(3))) void*)&As[stage][(wave * ACH + i) * 512]),
+                    a_off[i] + k0 * 2);
+    // W: a descriptor per stage (k rows k0 .. k0 + 63 of this column block)
+    const u32x4 wrs = raw_rsrc(Wg + (int64_t)k0 * P.ldw, (uint32_t)(BK * P.ldw * 2));
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      wreg[r] = *(const wrow_t*)(Wg + (int64_t)(k0 + w_kg * 4 + r) * P.ldw + n0 + w_nq * VN);
+    for (int i = 0; i < WCH; ++i)
+      load_lds_b128(wrs,
+                    __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+                        __attribute__((address_space(3))) void*)&Ws[stage][(wave * WCH + i) * 512]),
+                    w_off[i]);
   };
-  auto swrite = [&](int buf) {
+
+  // fragments: Aᵀ (MFMA B operand) for m block j, 16-k step ks
+  auto afrag = [&](int buf, int j, int ks) {
+    const int m = wm * WTM + j * 32 + l32;
+    return *(const u32x4*)&As[buf][m * BK + (((2 * ks + hi) ^ a_swz(m)) * 8)];
+  };
+  // Wᵀ (MFMA A operand) for n block i, 16-k step ks: lane l32 = column n,
+  // k = 8·hi + 0..7, from two transposing reads of 4 k rows each (lane i16
+  // of a 16-lane group points at row i16 / 4 and at columns 4·(i16 % 4)..+3)
+  auto wfrag = [&](int buf, int i, int ks) {
+    u32x4 r;
 #pragma unroll
-    for (int r = 0; r < ACH; ++r) {
-      const int ch = tid + r * 256;
-      *(u32x4*)&As[buf][(ch / (BK / 8)) * AST + (ch % (BK / 8)) * 8] = areg[r];
+    for (int e = 0; e < 2; ++e) {
+      const int k = ks * 16 + 8 * hi + 4 * e + (i16 >> 2);
+      const int n = wn * WTN + i * 32 + 16 * g16 + 4 * (i16 & 3);
+      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)&Ws[buf][k * TN + (((n >> 3) ^ w_swz(k)) * 8) + (n & 7)]);
+      const u32x2 w = __builtin_bit_cast(u32x2, v);
+      r[2 * e] = w[0];
+      r[2 * e + 1] = w[1];
     }
-#pragma unroll
-    for (int nn = 0; nn < VN; ++nn) {
-      const int sh = (nn & 1) * 16;
-      const uint32_t e0 = (wreg[0][nn >> 1] >> sh) & 0xFFFFu;
-      const uint32_t e1 = (wreg[1][nn >> 1] >> sh) & 0xFFFFu;
-      const uint32_t e2 = (wreg[2][nn >> 1] >> sh) & 0xFFFFu;
-      const uint32_t e3 = (wreg[3][nn >> 1] >> sh) & 0xFFFFu;
-      *(u32x2*)&Ws[buf][(w_nq * VN + nn) * AST + w_kg * 4] = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
-    }
+    return r;
   };
 
   f32x16 acc[WN][WM];
@@ -98,35 +153,49 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < WM; ++j) acc[i][j] = f32x16{};
 
+  // Loads run NSTAGE - 1 stages ahead.  Before each barrier a wave waits
+  // until its loads of the next stage have landed; the ones issued for
+  // later stages (ACH + WCH instructions each) may stay in flight.
+  constexpr int PER = ACH + WCH;
+  auto wait_next = [&](int ahead) {  // ahead = stages issued beyond the next one
+    if (ahead >= 2 && NSTAGE >= 4)
+      __builtin_amdgcn_s_waitcnt(0x0070 | ((2 * PER) & 15) | (((2 * PER) >> 4) << 14));
+    else if (ahead >= 1 && NSTAGE >= 3)
+      __builtin_amdgcn_s_waitcnt(0x0070 | (PER & 15) | ((PER >> 4) << 14));
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  };
   const int nk = g.K / BK;
-  gload(0);
-  swrite(0);
-  __syncthreads();
+#pragma unroll
+  for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
+    if (s0 < nk) gload(s0, s0);
+  wait_next(min(nk - 1, NSTAGE - 1) - 1);
+  asm volatile("s_barrier" ::: "memory");
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    const int buf = kt % NSTAGE;
+    // stage (kt - 1) % NSTAGE was last read in step kt - 1, which every wave has left
+    if (kt + NSTAGE - 1 < nk) gload(kt + NSTAGE - 1, (kt + NSTAGE - 1) % NSTAGE);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      u32x4 af[WN], bf[WM];
+      u32x4 wf[WN], af[WM];
+#pragma unroll
+      for (int i = 0; i < WN; ++i) wf[i] = wfrag(buf, i, ks);
+#pragma unroll
+      for (int j = 0; j < WM; ++j) af[j] = afrag(buf, j, ks);
 #pragma unroll
       for (int i = 0; i < WN; ++i)
-        af[i] = *(const u32x4*)&Ws[buf][(wn * (TN / 2) + i * 32 + l32) * AST + ks * 16 + hi * 8];
 #pragma unroll
-      for (int j = 0; j < WM; ++j)
-        bf[j] = *(const u32x4*)&As[buf][(wm * (TM / 2) + j * 32 + l32) * AST + ks * 16 + hi * 8];
-#pragma unroll
-      for (int i = 0; i < WN; ++i)
-#pragma unroll
-        for (int j = 0; j < WM; ++j) acc[i][j] = mfma_32x32x16<DT>(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < WM; ++j) acc[i][j] = mfma_32x32x16<DT>(wf[i], af[j], acc[i][j]);
     }
-    if (kt + 1 < nk) swrite(buf ^ 1);
-    __syncthreads();
+    // stage kt + 1 landed, this stage's reads done (lgkmcnt 0)
+    wait_next(min(nk - 1, kt + NSTAGE - 1) - (kt + 1));
+    asm volatile("s_barrier" ::: "memory");
   }
 
   uint16_t* Cg = (uint16_t*)P.C;
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
-    const int m = m0 + wm * (TM / 2) + j * 32 + l32;
+    const int m = m0 + wm * WTM + j * 32 + l32;
     if (m >= P.M) continue;
     const int bb = m / P.rows_per_b, tt = m % P.rows_per_b;
     uint16_t* crow = Cg + (int64_t)bb * P.c_sb + (int64_t)tt * P.c_st;
@@ -134,7 +203,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < WN; ++i)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int n = n0 + wn * (TN / 2) + i * 32 + gq * 8 + hi * 4;
+        const int n = n0 + wn * WTN + i * 32 + gq * 8 + hi * 4;
         const int head = n / P.head_dim, jj = n % P.head_dim;
         const u32x2 w = {pack2<DT>(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]),
                          pack2<DT>(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3])};
@@ -143,7 +212,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int DT, int TM, int TN>
+template <int DT, int TM, int TN, int WTM, int WTN, int NSTAGE>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   int max_tiles = 0;
   for (int i = 0; i < a.nprob; ++i) {
@@ -151,17 +220,25 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
     max_tiles = t > max_tiles ? t : max_tiles;
   }
   if (max_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<DT, TM, TN>), dim3(max_tiles, a.nprob), dim3(256), 0, st, a);
+  constexpr int threads = (TM / WTM) * (TN / WTN) * 64;
+  hipLaunchKernelGGL((gemm_kernel<DT, TM, TN, WTM, WTN, NSTAGE>), dim3(max_tiles, a.nprob), dim3(threads), 0,
+                     st, a);
   return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_dt(const GemmArgs& a, hipStream_t st) {
-  // Large tiles when they still give every CU at least two workgroups.
-  int64_t big = 0;
-  for (int i = 0; i < a.nprob; ++i) big += ((a.prob[i].M + 127) / 128) * (int64_t)(a.N / 128);
-  if (a.N % 128 == 0 && big >= 512) return launch_t<DT, 128, 128>(a, st);
-  return launch_t<DT, 64, 64>(a, st);
+  // The largest tile that still gives every CU a workgroup: bigger tiles
+  // load fewer bytes per flop.
+  auto tiles = [&](int tm, int tn) {
+    int64_t t = 0;
+    for (int i = 0; i < a.nprob; ++i) t += ((a.prob[i].M + tm - 1) / tm) * (int64_t)(a.N / tn);
+    return t;
+  };
+  if (GEMM_HUGE && a.N % 128 == 0 && tiles(256, 128) >= GEMM_BIG_MIN)
+    return launch_t<DT, 256, 128, 64, 64, 2>(a, st);  // measured slower so far: off by default
+  if (a.N % 128 == 0 && tiles(128, 128) >= GEMM_BIG_MIN) return launch_t<DT, 128, 128, 64, 64, GEMM_STAGES_128>(a, st);
+  return launch_t<DT, 64, 64, 32, 32, GEMM_STAGES_64>(a, st);
 }
 
 }  // namespace

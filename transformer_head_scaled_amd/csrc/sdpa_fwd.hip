@@ -41,8 +41,8 @@
 // weight is ≤ 2^8) the tile is accepted as is.  Otherwise -- and on the
 // first tile of a wave -- the wave takes the exact path: row max, new m,
 // rescale of O and l by exp2((m_old − m_new)·c), and the weights again.
-// The row sums are accumulated from the rounded weights (one dot2 per pair),
-// the same values P·V uses.
+// The row sums add the fp32 weights (P·V uses them rounded to the input
+// dtype; the two differ by at most 2^-9 relative per weight).
 //
 // Loads.  K and V tiles go from memory straight into LDS (buffer loads with
 // an LDS destination), with 16-byte chunks of each 128-byte row permuted
@@ -66,37 +66,9 @@ namespace {
 
 constexpr int D = 64;  // head dimension d_k = d_v handled by this kernel
 
-// 16 bytes per lane from a raw buffer (descriptor rsrc, byte offset voff)
-// straight into LDS: lane i writes bytes [lds + 16i, lds + 16i + 16).  Out-of-
-// range offsets read as zero.  Written as inline assembly so that the
-// compiler does not treat every later LDS read as a possible alias of the
-// transfer and wait for it; the caller orders it with explicit waits and
-// barriers instead.  M0 (the LDS base of the transfer) is set here; nothing
-// else in these kernels reads M0, and the compiler treats it as reserved.
-__device__ __forceinline__ void load_lds_b128(u32x4 rsrc, uint32_t lds, uint32_t voff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(lds), "v"(voff), "s"(rsrc)
-      : "memory");
-}
-
-// Sum of the two half-precision weights packed in `w` added to acc (fp32).
-template <int DT>
-__device__ __forceinline__ float dot2_sum(uint32_t w, float acc) {
-  if constexpr (DT == DT_BF16) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
-  } else {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
-  }
-}
-
 // NW waves per workgroup, each owning 64 query rows (two blocks of 32).
 template <int DT, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sdpa_fwd_kernel(SdpaArgs p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1 ? 1 : 2, 2))) void sdpa_fwd_kernel(SdpaArgs p) {
   constexpr int QB = 2, BN = 64, NSTAGE = 2;
   constexpr int BM = NW * 32 * QB;  // query rows per workgroup
   constexpr int CPW = 8 / NW;       // 1 KB pieces of a K (or V) tile loaded per wave
@@ -175,14 +147,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // with an LDS destination: each wave instruction fills 1 KB = 8 keys, lane
   // i writing bytes [16i, 16i + 16)); every lane fetches the 16-byte chunk
   // that the permuted layout puts at its position.
-  uint32_t k_off[CPW], v_off[CPW];
+  // Piece r (= wave·CPW + i, 8 keys) of a tile: lane -> key 8r + lane / 8,
+  // LDS chunk lane % 8.  The K chunk permutation depends on the key through
+  // bits 1..3 = (4r + lane / 16) & 7, i.e. on the parity of r (CPW is even);
+  // the V one through bit 1 = (lane / 16) & 1 only.
+  uint32_t k_lane[2];
 #pragma unroll
-  for (int i = 0; i < CPW; ++i) {
-    const int q = (wave * CPW + i) * 64 + lane;  // LDS chunk this lane fills
-    const int key = q >> 3;
-    k_off[i] = (uint32_t)((key * p.k_sr + ((q & 7) ^ ((key >> 1) & 7)) * 8) * 2);
-    v_off[i] = (uint32_t)((key * p.v_sr + ((q & 7) ^ (((key >> 1) & 1) << 2)) * 8) * 2);
-  }
+  for (int par = 0; par < 2; ++par)
+    k_lane[par] = (uint32_t)(((lane >> 3) * p.k_sr + ((lane & 7) ^ ((4 * par + (lane >> 4)) & 7)) * 8) * 2);
+  const uint32_t v_lane =
+      (uint32_t)(((lane >> 3) * p.v_sr + ((lane & 7) ^ (((lane >> 4) & 1) << 2)) * 8) * 2);
   const uint32_t k_tile = (uint32_t)(BN * p.k_sr * 2), v_tile = (uint32_t)(BN * p.v_sr * 2);
 
   // issue this wave's two LDS-destination loads of K (or V) for one tile.
@@ -190,20 +164,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // the waves of a compute unit do not all queue their loads at once.
   auto gload_k = [&](int tile, int stage) {
 #pragma unroll
-    for (int i = 0; i < CPW; ++i)
+    for (int i = 0; i < CPW; ++i) {
+      const int r = wave * CPW + i;
       // (the destinations are per wave: readfirstlane makes them scalars)
       load_lds_b128(krs,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-                        __attribute__((address_space(3))) void*)&Ks[stage][(wave * CPW + i) * 512]),
-                    k_off[i] + tile * k_tile);
+                        __attribute__((address_space(3))) void*)&Ks[stage][r * 512]),
+                    k_lane[i & 1] + (uint32_t)(r * 8 * p.k_sr * 2) + tile * k_tile);
+    }
   };
   auto gload_v = [&](int tile, int stage) {
 #pragma unroll
-    for (int i = 0; i < CPW; ++i)
+    for (int i = 0; i < CPW; ++i) {
+      const int r = wave * CPW + i;
       load_lds_b128(vrs,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-                        __attribute__((address_space(3))) void*)&Vs[stage][(wave * CPW + i) * 512]),
-                    v_off[i] + tile * v_tile);
+                        __attribute__((address_space(3))) void*)&Vs[stage][r * 512]),
+                    v_lane + (uint32_t)(r * 8 * p.v_sr * 2) + tile * v_tile);
+    }
   };
   // K fragment (kb, st) of this lane: key kb·32 + l32, chunk 2·st + hi
   const int kx = (l32 >> 1) & 7;
@@ -252,16 +230,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // weights of key block kb of query block qi against the current reference
   // value; returns their partial row sum
+  // The row sum adds the fp32 weights with plain adds: a packed dot2 would
+  // be exact to the rounded P, but on gfx950 it does not issue alongside
+  // the matrix cores, while adds do.
   auto weights = [&](int qi, int kb, const f32x16& sv, uint32_t (&pw)[8]) {
-    float rs = 0.f;
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], c, -mc[qi]));
       const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], c, -mc[qi]));
       pw[i] = pack2<DT>(e0, e1);
-      rs = dot2_sum<DT>(pw[i], rs);
+      rs0 += e0;
+      rs1 += e1;
     }
-    return rs;
+    return rs0 + rs1;
   };
   // per-element mask of query block qi (diagonal and key-length boundary
   // tiles only)
@@ -354,7 +336,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);  // then VALU / transcendental
+      __builtin_amdgcn_sched_group_barrier(0x402, 14, 0);  // then VALU / transcendental
     }
     u32x4 vf[2][2][2];
 #pragma unroll
@@ -385,7 +367,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 14, 0);
     }
     settle(masked, 1, buf, kbase, p1, rs1);
 
@@ -538,22 +520,33 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
   }
 }
 
-// Workgroup size: 4 waves (256 rows) without the causal mask.  With it the
-// work of a row block grows with its index; 2 waves (128 rows) give twice
-// as many workgroups as fit at once, dispatched longest first, so the
-// hardware can even out the compute units.
-template <bool CAUSAL>
-constexpr int waves_per_wg() {
-  return CAUSAL ? 2 : 4;
+// Workgroup size (waves of 64 query rows).  Unmasked: 4 waves when that
+// still gives at least two workgroups per CU, else 2 (less idle padding on
+// short sequences).  Causal: the work of a row block grows with its index;
+// 2 waves, with neighbouring heads walking their row blocks in opposite
+// directions, even out the compute units.  One wave when a head has no
+// more than 64 query rows.
+int waves_per_wg(int64_t n_q, int64_t heads, bool causal) {
+  if (n_q <= 64) return 1;
+  if (causal) return 2;
+  return ((n_q + 255) / 256) * heads >= 512 ? 4 : 2;
 }
 
-template <int DT, bool CAUSAL>
-hipError_t launch_mfma(const SdpaArgs& a, hipStream_t st) {
-  constexpr int NW = waves_per_wg<CAUSAL>();
+template <int DT, bool CAUSAL, int NW>
+hipError_t launch_nw(const SdpaArgs& a, hipStream_t st) {
   const int64_t nqb = (a.n_q + NW * 64 - 1) / (NW * 64);
   const int64_t grid = nqb * a.B * a.H;
   hipLaunchKernelGGL((sdpa_fwd_kernel<DT, CAUSAL, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
+}
+
+template <int DT, bool CAUSAL>
+hipError_t launch_mfma(const SdpaArgs& a, hipStream_t st) {
+  switch (waves_per_wg(a.n_q, (int64_t)a.B * a.H, CAUSAL)) {
+    case 1: return launch_nw<DT, CAUSAL, 1>(a, st);
+    case 2: return launch_nw<DT, CAUSAL, 2>(a, st);
+    default: return launch_nw<DT, CAUSAL, 4>(a, st);
+  }
 }
 
 template <int DH>
@@ -565,8 +558,8 @@ hipError_t launch_f32(const SdpaArgs& a, float scale, int causal, hipStream_t st
 
 }  // namespace
 
-int sdpa_rows_per_workgroup(int dtype, int causal) {
-  return dtype == DT_F32 ? 64 : (causal ? waves_per_wg<true>() : waves_per_wg<false>()) * 64;
+int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t heads) {
+  return dtype == DT_F32 ? 64 : waves_per_wg(n_q, heads, causal != 0) * 64;
 }
 
 hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float scale, hipStream_t st) {
