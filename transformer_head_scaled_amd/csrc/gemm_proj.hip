@@ -175,23 +175,39 @@ __global__ __launch_bounds__((TM / WTM) * (TN / WTN) * 64) void gemm_kernel(Gemm
     const int buf = kt % NSTAGE;
     // stage (kt - 1) % NSTAGE was last read in step kt - 1, which every wave has left
     if (kt + NSTAGE - 1 < nk) gload(kt + NSTAGE - 1, (kt + NSTAGE - 1) % NSTAGE);
+    // fragments of the next 16-k step are read while this step's MFMAs run
+    u32x4 wf[2][WN], af[2][WM];
+#pragma unroll
+    for (int i = 0; i < WN; ++i) wf[0][i] = wfrag(buf, i, 0);
+#pragma unroll
+    for (int j = 0; j < WM; ++j) af[0][j] = afrag(buf, j, 0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      u32x4 wf[WN], af[WM];
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) {
 #pragma unroll
-      for (int i = 0; i < WN; ++i) wf[i] = wfrag(buf, i, ks);
+        for (int i = 0; i < WN; ++i) wf[cur ^ 1][i] = wfrag(buf, i, ks + 1);
 #pragma unroll
-      for (int j = 0; j < WM; ++j) af[j] = afrag(buf, j, ks);
+        for (int j = 0; j < WM; ++j) af[cur ^ 1][j] = afrag(buf, j, ks + 1);
+      }
 #pragma unroll
       for (int i = 0; i < WN; ++i)
 #pragma unroll
-        for (int j = 0; j < WM; ++j) acc[i][j] = mfma_32x32x16<DT>(wf[i], af[j], acc[i][j]);
+        for (int j = 0; j < WM; ++j) acc[i][j] = mfma_32x32x16<DT>(wf[cur][i], af[cur][j], acc[i][j]);
     }
     // stage kt + 1 landed, this stage's reads done (lgkmcnt 0)
     wait_next(min(nk - 1, kt + NSTAGE - 1) - (kt + 1));
     asm volatile("s_barrier" ::: "memory");
   }
 
+  // A 32-column block never straddles a head (head_dim is a multiple of
+  // 32), so the head split is computed once per block.
+  int64_t col_off[WN];
+#pragma unroll
+  for (int i = 0; i < WN; ++i) {
+    const int nb = n0 + wn * WTN + i * 32;
+    col_off[i] = (int64_t)(nb / P.head_dim) * P.c_sh + nb % P.head_dim + hi * 4;
+  }
   uint16_t* Cg = (uint16_t*)P.C;
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
@@ -203,11 +219,9 @@ __global__ __launch_bounds__((TM / WTM) * (TN / WTN) * 64) void gemm_kernel(Gemm
     for (int i = 0; i < WN; ++i)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int n = n0 + wn * WTN + i * 32 + gq * 8 + hi * 4;
-        const int head = n / P.head_dim, jj = n % P.head_dim;
         const u32x2 w = {pack2<DT>(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]),
                          pack2<DT>(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3])};
-        *(u32x2*)(crow + (int64_t)head * P.c_sh + jj) = w;
+        *(u32x2*)(crow + col_off[i] + gq * 8) = w;
       }
   }
 }
