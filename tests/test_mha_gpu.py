@@ -79,6 +79,7 @@ def test_workload_big_cross(dtype):
     (2, 33, 190, 512, 8, True, "none", [190, 1]),
     (1, 1, 1, 64, 1, False, "none", None),              # h = 1, d_model = 64
     (4, 130, 70, 128, 2, True, "none", None),
+    (3, 450, 450, 1024, 16, False, "none", [450, 200, 1]),  # 128 x 128 GEMM tiles, ragged rows
 ])
 def test_ragged(case):
     B, n_q, n_k, dm, h, cross, mask, lens = case

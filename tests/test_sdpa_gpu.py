@@ -88,6 +88,24 @@ def test_workload_long_b4_n4096_sampled(mask):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_four_wave_workgroups_ragged_lens(dtype):
+    """[8,16,1000,1000] with per-batch key lengths (0, 1, 63, 64, 500, 999,
+    1000, and one past n_k): enough row blocks for the 4-wave (256-row)
+    workgroups, with a ragged last row block and key-length boundary tiles.
+    One whole head per batch is compared."""
+    lens = [1000, 999, 500, 64, 63, 1, 0, 1100]
+    ins = synth.sdpa_inputs(31, 8, 16, 1000, 1000, 64, dtype=dtype)
+    note(f"sdpa {dtype} [8,16,1000,1000] key lengths {lens}")
+    got = _run(ins, dtype, "none", lens)
+    Q, K, V = (ins[n][1] for n in "QKV")
+    for b in range(8):
+        i = (5 * b) % 16
+        exp = oracle.sdpa(Q[b:b + 1, i:i + 1], K[b:b + 1, i:i + 1], V[b:b + 1, i:i + 1], 0.125,
+                          oracle.MASK_NONE, [lens[b]])[0, 0]
+        _check(got[b, i], exp, dtype, f"{dtype} 4-wave head ({b},{i}) len {lens[b]}")
+
+
 # ragged shapes: tails of the 128-row query blocks and 64-key tiles, tiny
 # sizes, cross-attention n_q != n_k, key padding including 0 and > n_k
 RAGGED = [
