@@ -82,28 +82,40 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
   // k), which keeps the transposing fragment reads conflict-free
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NSTAGE][BN * D];
 
-  const int nqb = (p.n_q + BM - 1) / BM;
+  // Rows.  Unmasked: workgroup qb of a head takes rows [qb·BM, qb·BM + BM),
+  // each wave 64 consecutive rows.  Causal: the work of a row grows with its
+  // index, so a wave takes the 32-row blocks u and nb − 1 − u of its head
+  // (u = its unit, nb the number of 32-row blocks rounded up to even): every
+  // wave then has about the same work and the two waves that share a SIMD
+  // run side by side until the end, instead of a long wave finishing alone.
+  const int nb32e = ((p.n_q + 31) / 32 + 1) & ~1;
+  const int units = nb32e / 2;  // causal: waves of work per head
+  const int nqb = CAUSAL ? (units + NW - 1) / NW : (p.n_q + BM - 1) / BM;
   const uint32_t total = (uint32_t)nqb * p.B * p.H;
   const uint32_t t = xcd_remap(blockIdx.x, total);
   const int bh = t / nqb;
-  int qb = t % nqb;
-  // Causal: the work of row block qb grows with qb.  Neighbouring heads
-  // walk their row blocks in opposite directions, so that the workgroups a
-  // compute unit receives (every 32nd of its XCD when they are dealt out
-  // in order) pair long row blocks with short ones.
-  if (CAUSAL && !(bh & 1)) qb = nqb - 1 - qb;
+  const int qb = t % nqb;
   const int b = bh / p.H, hh = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
 
   int n_eff = p.n_k;
   if (p.lens) n_eff = min(max(p.lens[b], 0), p.n_k);
-  const int q0 = qb * BM;
+  const int unit = qb * NW + wave;
+  const bool wave_active = !CAUSAL || unit < units;
+  int row0[QB];  // first row of each of this wave's two 32-row blocks
+  if (CAUSAL) {
+    row0[0] = 32 * unit;
+    row0[1] = 32 * (nb32e - 1 - unit);
+  } else {
+    row0[0] = qb * BM + wave * 64;
+    row0[1] = row0[0] + 32;
+  }
   int kend = n_eff;
-  if (CAUSAL) kend = min(kend, q0 + BM);
+  // causal: keys up to the last row of the workgroup's first wave (its
+  // upper block is the highest of the workgroup)
+  if (CAUSAL) kend = min(kend, 32 * (nb32e - qb * NW));
   const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
-  const int wave_q_first = q0 + wave * QB * 32;
-  const int wave_q_last = wave_q_first + QB * 32 - 1;
 
   const uint16_t* Qg = (const uint16_t*)p.Q + b * p.q_sb + hh * p.q_sh;
   const uint16_t* Kg = (const uint16_t*)p.K + b * p.k_sb + hh * p.k_sh;
@@ -122,7 +134,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
   u32x4 qf[QB][4];
 #pragma unroll
   for (int qi = 0; qi < QB; ++qi) {
-    const int row = wave_q_first + qi * 32 + l32;
+    const int row = row0[qi] + l32;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -248,7 +260,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
   // per-element mask of query block qi (diagonal and key-length boundary
   // tiles only)
   auto apply_mask = [&](int qi, int kbase, int kb, f32x16& sv) {
-    const int row = wave_q_first + qi * 32 + l32;
+    const int row = row0[qi] + l32;
     // visible iff the register's key offset in the tile (a constant) < lim
     int lim = (CAUSAL ? min(n_eff, row + 1) : n_eff) - kbase - 4 * hi;
     // opaque to the optimiser: otherwise it hoists one loop-invariant
@@ -382,9 +394,45 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
         }
   };
 
+  // One 64-key tile for block 1 only (causal: block 0 has no visible key
+  // left).
+  auto tile_hi = [&](auto masked, int buf, int kbase, auto&& mid) {
+    constexpr bool MASKED = decltype(masked)::value;
+    f32x16 s1[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s1[kb] = scores(std::false_type{}, 1, buf, kbase, kb);
+    mid();
+    u32x4 vf[2][2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+          vf[kb][t2][db] = vfrag(buf, kb, t2, db);
+    if constexpr (MASKED) {
+      apply_mask(1, kbase, 0, s1[0]);
+      apply_mask(1, kbase, 1, s1[1]);
+    }
+    uint32_t p1[2][8];
+    const float rs1 = weights(1, 0, s1[0], p1[0]) + weights(1, 1, s1[1], p1[1]);
+    settle(masked, 1, buf, kbase, p1, rs1);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const u32x4 bv = {p1[kb][4 * t2], p1[kb][4 * t2 + 1], p1[kb][4 * t2 + 2], p1[kb][4 * t2 + 3]};
+          o[1][db] = mfma_32x32x16<DT>(vf[kb][t2][db], bv, o[1][db]);
+        }
+  };
+
   // One step of the key loop: start the loads of tile j + NSTAGE - 1,
-  // compute tile j, barrier.
-  auto step = [&](int j, auto masked) {
+  // compute tile j (both blocks, block 1 only, or nothing), barrier.
+  // WHAT: 0 = nothing, 1 = block 1 only, 2 = both blocks.
+  auto step = [&](int j, auto masked, auto what) {
+    constexpr int WHAT = decltype(what)::value;
     const int buf = j % NSTAGE;
     const bool more = j + NSTAGE - 1 < ntiles;
     if (more) gload_k(j + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE);
@@ -392,9 +440,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
       if (more) gload_v(j + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE);
     };
     const int kbase = j * BN;
-    // causal: tiles wholly above this wave's rows are skipped
-    if (!decltype(masked)::value || !CAUSAL || kbase <= wave_q_last)
+    if constexpr (WHAT == 2)
       tile(masked, buf, kbase, load_v);
+    else if constexpr (WHAT == 1)
+      tile_hi(masked, buf, kbase, load_v);
     else
       load_v();
     // Before the barrier, this wave's loads of tile j + 1 have landed: only
@@ -406,23 +455,47 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
   };
-  // Tiles before jd need no per-element mask: they lie below this wave's
-  // diagonal (causal) and inside the valid keys.  Two loops, so that each
-  // holds one variant of the tile code.  Every wave still takes part in
-  // all ntiles barriers.
-  int jd = min(n_eff / BN, ntiles);
-  if (CAUSAL) jd = min(jd, wave_q_first / BN);
+  // The key loop in phases, one loop per variant of the tile code (a shared
+  // loop makes the compiler keep copies of the accumulators).  Every wave
+  // takes part in all ntiles barriers.
+  using no = std::false_type;
+  using yes = std::true_type;
+  const int nfull = min(n_eff / BN, ntiles);  // tiles inside the valid keys
   int j = 0;
-  for (; j < jd; ++j) step(j, std::false_type{});
-  for (; j < ntiles; ++j) step(j, std::true_type{});
+  if (!CAUSAL) {
+    for (; j < nfull; ++j) step(j, no{}, std::integral_constant<int, 2>{});
+    for (; j < ntiles; ++j) step(j, yes{}, std::integral_constant<int, 2>{});
+  } else {
+    // per block: the first tile that needs the mask, the last with a
+    // visible key (an upper block past the last query row has none)
+    int fm[QB], lt[QB];
+#pragma unroll
+    for (int qi = 0; qi < QB; ++qi) {
+      fm[qi] = min((row0[qi] + 1) / BN, nfull);
+      lt[qi] = min((row0[qi] + 31) / BN, ntiles - 1);
+    }
+    if (row0[1] >= p.n_q) lt[1] = -1;
+    int end_a = 0, end_b = 0, end_c = 0, end_d = 0;
+    if (wave_active) {
+      end_a = min(fm[0], fm[1]);            // both blocks, no mask
+      end_b = max(end_a, lt[0] + 1);        // both, masked: up to block 0's diagonal
+      end_c = max(end_b, fm[1]);            // block 1 only, no mask
+      end_d = max(end_c, lt[1] + 1);        // block 1 only, masked
+    }
+    for (; j < end_a; ++j) step(j, no{}, std::integral_constant<int, 2>{});
+    for (; j < end_b; ++j) step(j, yes{}, std::integral_constant<int, 2>{});
+    for (; j < end_c; ++j) step(j, no{}, std::integral_constant<int, 1>{});
+    for (; j < end_d; ++j) step(j, yes{}, std::integral_constant<int, 1>{});
+    for (; j < ntiles; ++j) step(j, no{}, std::integral_constant<int, 0>{});
+  }
 
   // ---- normalise and store this lane's query row (4 consecutive d per store)
 #pragma unroll
   for (int qi = 0; qi < QB; ++qi) {
     const float L = pair_sum(l[qi]);
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    const int row = wave_q_first + qi * 32 + l32;
-    if (row < p.n_q) {
+    const int row = row0[qi] + l32;
+    if (wave_active && row < p.n_q) {
       uint16_t* orow = Og + (int64_t)row * p.o_sr;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
@@ -520,21 +593,20 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
   }
 }
 
-// Workgroup size (waves of 64 query rows).  Unmasked: 4 waves when that
-// still gives at least two workgroups per CU, else 2 (less idle padding on
-// short sequences).  Causal: the work of a row block grows with its index;
-// 2 waves, with neighbouring heads walking their row blocks in opposite
-// directions, even out the compute units.  One wave when a head has no
-// more than 64 query rows.
-int waves_per_wg(int64_t n_q, int64_t heads, bool causal) {
+// Workgroup size (waves of 64 query rows): 4 waves when that still gives at
+// least two workgroups per CU, else 2 (less idle padding on short
+// sequences); one wave when a head has no more than 64 query rows.  The
+// same for both masks (causal waves carry equal work by construction).
+int waves_per_wg(int64_t n_q, int64_t heads, bool /*causal*/) {
   if (n_q <= 64) return 1;
-  if (causal) return 2;
   return ((n_q + 255) / 256) * heads >= 512 ? 4 : 2;
 }
 
 template <int DT, bool CAUSAL, int NW>
 hipError_t launch_nw(const SdpaArgs& a, hipStream_t st) {
-  const int64_t nqb = (a.n_q + NW * 64 - 1) / (NW * 64);
+  // causal: one wave per pair of 32-row blocks (see the kernel)
+  const int64_t units = ((a.n_q + 31) / 32 + 1) / 2;
+  const int64_t nqb = CAUSAL ? (units + NW - 1) / NW : (a.n_q + NW * 64 - 1) / (NW * 64);
   const int64_t grid = nqb * a.B * a.H;
   hipLaunchKernelGGL((sdpa_fwd_kernel<DT, CAUSAL, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
