@@ -83,10 +83,12 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json, commands):
         wb = w.get(name, 0.0) * 1024.0 * write_factor
         res["kernels"][name] = {"fetch_kib": f[name], "write_kib": w.get(name),
                                 "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
-        if ", false," in name:
-            res["noncausal_bytes_per_launch"] = fb + wb
-        elif ", true," in name:
-            res["causal_bytes_per_launch"] = fb + wb
+    # the bench workload is the largest launch of each mode (smaller SDPA
+    # launches of other workloads may be in the same run)
+    for mode, tag in (("noncausal", ", false,"), ("causal", ", true,")):
+        cands = [v["bytes_per_launch"] for k, v in res["kernels"].items() if tag in k]
+        if cands:
+            res[mode + "_bytes_per_launch"] = max(cands)
     with open(out_json, "w") as fh:
         json.dump(res, fh, indent=1)
         fh.write("\n")
