@@ -44,6 +44,15 @@ constexpr int BK = 64;  // k per LDS stage (four 16-k MFMA steps); A rows are 12
 #ifndef GEMM_HUGE
 #define GEMM_HUGE 0
 #endif
+#ifndef GEMM_WTM_128
+#define GEMM_WTM_128 64  // per-wave tile of the 128 x 128 workgroup tile
+#endif
+#ifndef GEMM_WTN_128
+#define GEMM_WTN_128 64
+#endif
+#ifndef GEMM_STAGES_HUGE
+#define GEMM_STAGES_HUGE 2
+#endif
 #ifndef GEMM_BIG_MIN
 #define GEMM_BIG_MIN 256   // 128 x 128 tiles once there are enough to give each CU one
 #endif
@@ -250,8 +259,9 @@ hipError_t launch_dt(const GemmArgs& a, hipStream_t st) {
     return t;
   };
   if (GEMM_HUGE && a.N % 128 == 0 && tiles(256, 128) >= GEMM_BIG_MIN)
-    return launch_t<DT, 256, 128, 64, 64, 2>(a, st);  // measured slower so far: off by default
-  if (a.N % 128 == 0 && tiles(128, 128) >= GEMM_BIG_MIN) return launch_t<DT, 128, 128, 64, 64, GEMM_STAGES_128>(a, st);
+    return launch_t<DT, 256, 128, 64, 64, GEMM_STAGES_HUGE>(a, st);  // measured slower so far: off by default
+  if (a.N % 128 == 0 && tiles(128, 128) >= GEMM_BIG_MIN)
+    return launch_t<DT, 128, 128, GEMM_WTM_128, GEMM_WTN_128, GEMM_STAGES_128>(a, st);
   return launch_t<DT, 64, 64, 32, 32, GEMM_STAGES_64>(a, st);
 }
 
