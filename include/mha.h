@@ -78,8 +78,11 @@ enum {
  *   seq_lens[b] keys (key padding; clamped to [0, n_k]).  Masked K/V rows
  *   are never read, so their contents (NaN included) have no effect.
  * scale: any finite float; the pages use 1/sqrt(d_k).
- * Supported: BF16/F16 with d_k = d_v = 64 and n_k·64·2 bytes < 2 GiB (MFMA
- *   flash kernel); F32 with d_k = d_v in {16, 32, 64, 128}.
+ * Supported: BF16/F16 with d_k = d_v in {16, 32, 64, 128} and n_k·d_k·2
+ *   bytes < 2 GiB (MFMA flash kernel); F32 with d_k = d_v in {16, 32, 64,
+ *   128}.  The head-dimension variants are those of [N] Table 3 row (A)
+ *   (d_model fixed, h and d_k = d_model / h varied); d_k = 512 (h = 1) is
+ *   not supported.
  * O must not overlap Q, K, V or seq_lens (MHA_ERR_ALIAS).
  */
 int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype, int64_t B,
@@ -101,7 +104,8 @@ int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype
  *                                     owns columns [i·d_k, (i+1)·d_k)
  *   Wo [h·d_k, d_model]               row blocks in the same head order
  *   out [B, n_q, d_model]             (written)
- * d_k = d_v = d_model / h.  Supported: BF16/F16 with d_k = 64.
+ * d_k = d_v = d_model / h.  Supported: BF16/F16 with d_k in {16, 32, 64,
+ *   128} and d_model a multiple of 64.
  * mask_kind: NONE (encoder self / cross) or CAUSAL (decoder self).
  * kv_lens: NULL or device int32[B], key padding as in mha_sdpa.
  * workspace: device memory of at least mha_forward_workspace_size() bytes,

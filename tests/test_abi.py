@@ -58,7 +58,8 @@ def _sdpa(dtype=M.MHA_BF16, B=1, h=1, n_q=8, n_k=8, d_k=64, d_v=64, scale=0.125,
     (dict(n_k=9, mask=M.MHA_MASK_CAUSAL), M.MHA_ERR_SHAPE),
     (dict(scale=float("nan")), M.MHA_ERR_INVALID_ARG),
     (dict(scale=float("inf")), M.MHA_ERR_INVALID_ARG),
-    (dict(d_k=128, d_v=128), M.MHA_ERR_UNSUPPORTED),
+    (dict(d_k=256, d_v=256), M.MHA_ERR_UNSUPPORTED),
+    (dict(d_k=48, d_v=48), M.MHA_ERR_UNSUPPORTED),
     (dict(d_k=64, d_v=32), M.MHA_ERR_UNSUPPORTED),
     (dict(dtype=M.MHA_F32, d_k=48, d_v=48), M.MHA_ERR_UNSUPPORTED),
     (dict(Q=None), M.MHA_ERR_INVALID_ARG),
@@ -98,7 +99,9 @@ def _fwd(dtype=M.MHA_BF16, B=2, n_q=8, n_k=8, d_model=128, h=2, mask=M.MHA_MASK_
     (dict(dtype=5), M.MHA_ERR_DTYPE),
     (dict(dtype=M.MHA_F32), M.MHA_ERR_UNSUPPORTED),
     (dict(d_model=129, h=2), M.MHA_ERR_SHAPE),
-    (dict(d_model=256, h=2), M.MHA_ERR_UNSUPPORTED),     # head dim 128
+    (dict(d_model=512, h=2), M.MHA_ERR_UNSUPPORTED),     # head dim 256
+    (dict(d_model=96, h=2), M.MHA_ERR_UNSUPPORTED),      # head dim 48
+    (dict(d_model=96, h=3), M.MHA_ERR_UNSUPPORTED),      # head dim 32, d_model not a multiple of 64
     (dict(h=0), M.MHA_ERR_SHAPE),
     (dict(n_k=9), M.MHA_ERR_SHAPE),                       # self-attention, n_k != n_q
     (dict(n_k=9, x_kv=0x600000, mask=M.MHA_MASK_CAUSAL), M.MHA_ERR_SHAPE),

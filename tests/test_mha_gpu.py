@@ -90,6 +90,24 @@ def test_ragged(case):
     _check(got, _oracle(ins, h, mask, lens), dtype, f"ragged {case}")
 
 
+@pytest.mark.parametrize("case", [
+    # (B, n_q, n_k, d_model, h, cross, mask, lens): the head splits of
+    # Table 3 rows (A) and (C) of the nickwang.xyz page
+    (2, 100, 100, 512, 32, False, "causal", None),      # d_k = 16
+    (3, 70, 130, 512, 16, True, "none", [130, 64, 1]),  # d_k = 32
+    (2, 150, 150, 512, 4, False, "none", [150, 9]),     # d_k = 128
+    (2, 200, 200, 1024, 8, False, "causal", None),      # d_model 1024, d_k = 128
+    (2, 64, 64, 256, 8, False, "none", None),           # d_model 256, d_k = 32
+])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_head_dims(case, dtype):
+    B, n_q, n_k, dm, h, cross, mask, lens = case
+    ins = synth.mha_inputs(250 + n_q + h, B, n_q, n_k, dm, h, cross, dtype=dtype)
+    note(f"forward {dtype} head dim {dm // h} {case}")
+    got = _run(ins, dtype, h, mask, lens, True)
+    _check(got, _oracle(ins, h, mask, lens), dtype, f"head dim {dm // h} {case}")
+
+
 def test_single_head_equals_sdpa_chain():
     """h = 1 (Table 3 (A) of the nickwang.xyz page): one head of full width
     d_k = d_model, so the sublayer is one attention with scale 1/√d_model

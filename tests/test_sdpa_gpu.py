@@ -142,6 +142,51 @@ def test_f32_head_dims(d):
     _check(got, exp, "f32", f"f32 d={d}")
 
 
+# Head dimensions of Table 3 rows (A) and (C) of the nickwang.xyz page
+# (d_model fixed, h and d_k = d_v = d_model / h varied): the MFMA kernel for
+# each, on one- and two-wave workgroups, with ragged query blocks and key
+# tiles, key padding (0, 1, past n_k) and both masks.
+HEAD_DIM_CASES = [
+    # (B, h, n_q, n_k, mask, lens)
+    (3, 2, 50, 90, "none", [90, 7, 0]),
+    (2, 3, 200, 200, "causal", [150, 200]),
+    (2, 2, 257, 130, "none", [130, 1]),
+    (1, 3, 129, 129, "causal", None),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [16, 32, 128])
+@pytest.mark.parametrize("case", HEAD_DIM_CASES,
+                         ids=lambda c: "x".join(map(str, c[:4])) + f"_{c[4]}" + ("_lens" if c[5] else ""))
+def test_head_dims(dtype, d, case):
+    B, h, n_q, n_k, mask, lens = case
+    scale = 1 / math.sqrt(d)
+    ins = synth.sdpa_inputs(300 + d + n_q, B, h, n_q, n_k, d, dtype=dtype)
+    note(f"sdpa {dtype} d={d} {case}")
+    got = _run(ins, dtype, mask, lens, scale=scale)
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], scale, MASKS[mask], lens)
+    _check(got, exp, dtype, f"{dtype} d={d} {case}")
+
+
+@pytest.mark.parametrize("d", [16, 32, 128])
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_head_dims_four_wave(d, mask):
+    """[8,16,1000,1000] bf16 with per-batch key lengths: four-wave
+    workgroups for each head dimension; one whole head per batch."""
+    lens = [1000, 999, 500, 64, 63, 1, 0, 1100]
+    scale = 1 / math.sqrt(d)
+    ins = synth.sdpa_inputs(330 + d, 8, 16, 1000, 1000, d, dtype="bf16")
+    note(f"sdpa bf16 d={d} {mask} [8,16,1000,1000] key lengths {lens}")
+    got = _run(ins, "bf16", mask, lens, scale=scale)
+    Q, K, V = (ins[n][1] for n in "QKV")
+    for b in range(8):
+        i = (3 * b + 1) % 16
+        exp = oracle.sdpa(Q[b:b + 1, i:i + 1], K[b:b + 1, i:i + 1], V[b:b + 1, i:i + 1], scale,
+                          MASKS[mask], [lens[b]])[0, 0]
+        _check(got[b, i], exp, "bf16", f"d={d} {mask} head ({b},{i}) len {lens[b]}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 1.0])
 def test_unusual_scales(dtype, scale):

@@ -209,14 +209,18 @@ __global__ __launch_bounds__((TM / WTM) * (TN / WTN) * 64) void gemm_kernel(Gemm
     asm volatile("s_barrier" ::: "memory");
   }
 
-  // A 32-column block never straddles a head (head_dim is a multiple of
-  // 32), so the head split is computed once per block.
+  // The head split is computed once per 32-column block.  A lane stores
+  // columns 8·gq + 4·hi .. +3 of the block; with head_dim a multiple of 32
+  // they all belong to the block's head, with head_dim 16 the block holds
+  // two heads and gq >= 2 falls in the second (head_dim is 16 or a multiple
+  // of 32).
   int64_t col_off[WN];
 #pragma unroll
   for (int i = 0; i < WN; ++i) {
     const int nb = n0 + wn * WTN + i * 32;
     col_off[i] = (int64_t)(nb / P.head_dim) * P.c_sh + nb % P.head_dim + hi * 4;
   }
+  const int64_t half_step = P.head_dim == 16 ? P.c_sh : 16;  // offset of columns 16..31
   uint16_t* Cg = (uint16_t*)P.C;
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
@@ -230,7 +234,7 @@ __global__ __launch_bounds__((TM / WTM) * (TN / WTN) * 64) void gemm_kernel(Gemm
       for (int gq = 0; gq < 4; ++gq) {
         const u32x2 w = {pack2<DT>(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]),
                          pack2<DT>(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3])};
-        *(u32x2*)(crow + col_off[i] + gq * 8) = w;
+        *(u32x2*)(crow + col_off[i] + (gq >> 1) * half_step + (gq & 1) * 8) = w;
       }
   }
 }

@@ -31,7 +31,7 @@ int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t heads);
 //   C + (m / rows_per_b) * c_sb + (m % rows_per_b) * c_st
 //     + (n / head_dim) * c_sh + (n % head_dim)
 // which expresses both the head-split layout [B, h, n, d] and a plain
-// row-major [M, N] matrix.
+// row-major [M, N] matrix.  head_dim is 16 or a multiple of 32.
 struct GemmProblem {
   const void* A;
   const void* W;

@@ -124,8 +124,8 @@ int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype
   if (dtype == MHA_F32) {
     if (d_k != d_v || (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128))
       return fail(MHA_ERR_UNSUPPORTED, "mha_sdpa: f32 needs d_k == d_v in {16,32,64,128}");
-  } else if (d_k != 64 || d_v != 64) {
-    return fail(MHA_ERR_UNSUPPORTED, "mha_sdpa: bf16/f16 needs d_k == d_v == 64");
+  } else if (d_k != d_v || (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128)) {
+    return fail(MHA_ERR_UNSUPPORTED, "mha_sdpa: bf16/f16 needs d_k == d_v in {16,32,64,128}");
   } else if (n_k * d_k * 2 > kMaxBufferBytes) {
     return fail(MHA_ERR_UNSUPPORTED, "mha_sdpa: one head's K/V exceeds 2 GiB (n_k %lld)",
                 (long long)n_k);
@@ -206,7 +206,12 @@ int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* W
     return fail(MHA_ERR_SHAPE, "mha_forward: causal mask needs n_q == n_k");
   if (dtype == MHA_F32) return fail(MHA_ERR_UNSUPPORTED, "mha_forward: f32 is not implemented");
   const int64_t d = d_model / h;
-  if (d != 64) return fail(MHA_ERR_UNSUPPORTED, "mha_forward: head dim %lld (needs 64)", (long long)d);
+  if (d != 16 && d != 32 && d != 64 && d != 128)
+    return fail(MHA_ERR_UNSUPPORTED, "mha_forward: head dim %lld (needs 16, 32, 64 or 128)",
+                (long long)d);
+  if (d_model % 64 != 0)  // the projection GEMMs tile N and K by 64
+    return fail(MHA_ERR_UNSUPPORTED, "mha_forward: d_model %lld is not a multiple of 64",
+                (long long)d_model);
   if (n_k * d * 2 > kMaxBufferBytes)
     return fail(MHA_ERR_UNSUPPORTED, "mha_forward: one head's K/V exceeds 2 GiB (n_k %lld)",
                 (long long)n_k);

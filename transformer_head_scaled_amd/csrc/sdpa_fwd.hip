@@ -64,22 +64,46 @@ namespace mha {
 
 namespace {
 
-constexpr int D = 64;  // head dimension d_k = d_v handled by this kernel
+// K-row chunk permutation for head dimension D (16-byte chunks, D / 8 of
+// them per row): chunk c of key k is stored at c ^ kswz<D>(k).  A fragment
+// read of 16 lanes covers 16 consecutive keys at one chunk index; 256 bytes
+// of LDS span all 64 banks, i.e. 256 / (2·D) rows, and the permutation
+// spreads the 16 keys over the 16 different 16-byte bank groups.
+template <int D>
+__host__ __device__ constexpr int kswz(int key) {
+  return (key / (128 / D)) & (D / 8 - 1);
+}
+// V-row chunk permutation: a transposing read phase of 32 lanes covers 4
+// consecutive keys (aligned to 4) × 32 columns = 4 × 64 bytes, which must
+// land in different quarters of the 256-byte bank cycle.
+template <int D>
+__host__ __device__ constexpr int vswz(int key) {
+  return D == 128 ? 4 * (key & 3) : D == 64 ? 4 * ((key >> 1) & 1) : 0;
+}
 
-// NW waves per workgroup, each owning 64 query rows (two blocks of 32).
-template <int DT, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1 ? 1 : 2, 2))) void sdpa_fwd_kernel(SdpaArgs p) {
+// NW waves per workgroup, each owning 64 query rows (two blocks of 32), for
+// head dimension DH = d_k = d_v in {16, 32, 64, 128}.  With DH = 128 the
+// accumulators need more than 256 registers, so one wave per SIMD.
+template <int DT, int DH, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 1 || DH > 64) ? 1 : 2, 2))) void sdpa_fwd_kernel(SdpaArgs p) {
+  constexpr int D = DH;
   constexpr int QB = 2, BN = 64, NSTAGE = 2;
   constexpr int BM = NW * 32 * QB;  // query rows per workgroup
-  constexpr int CPW = 8 / NW;       // 1 KB pieces of a K (or V) tile loaded per wave
+  constexpr int NST = D / 16;       // 16-deep MFMA steps of a score block
+  constexpr int NDB = D >= 32 ? D / 32 : 1;  // 32-row blocks of Oᵀ (d = 16: one, half used)
+  constexpr int CR = D / 8;         // 16-byte chunks per K/V row
+  constexpr int KPP = 64 / CR;      // keys per 1 KB piece of a tile
+  constexpr int PIECES = BN / KPP;  // 1 KB pieces per K (or V) tile
+  constexpr int CPW = PIECES >= NW ? PIECES / NW : 1;  // pieces loaded per (loading) wave
+  constexpr int NKL = CR >= 8 ? CR / 4 : 1;  // distinct per-lane K offsets (by piece)
+  static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head dimension");
+  static_assert(CPW % NKL == 0, "a wave's first piece must start a K offset cycle");
   constexpr float kAccept = 256.f;  // accept a tile while partial row sums are <= 2^8
 
-  // K tile: [key][64], 128-byte rows whose eight 16-byte chunks are
-  // permuted per row (chunk c of key k sits at c ^ ((k >> 1) & 7)), so the
-  // 16 lanes of a fragment read hit 16 different bank groups
+  // K tile: [key][D], rows of D / 8 16-byte chunks permuted by kswz
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NSTAGE][BN * D];
-  // V tile: [key][64], 128-byte rows, chunk c of key k at c ^ (4 · bit 1 of
-  // k), which keeps the transposing fragment reads conflict-free
+  // V tile: [key][D], chunks permuted by vswz, which keeps the transposing
+  // fragment reads conflict-free
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NSTAGE][BN * D];
 
   // Rows.  Unmasked: workgroup qb of a head takes rows [qb·BM, qb·BM + BM),
@@ -131,24 +155,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
                      (uint32_t)((int64_t)n_eff * p.v_sr * 2), 0x00020000u};
 
   // ---- Q fragments (B operand), resident for the whole kernel
-  u32x4 qf[QB][4];
+  u32x4 qf[QB][NST];
 #pragma unroll
   for (int qi = 0; qi < QB; ++qi) {
     const int row = row0[qi] + l32;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < NST; ++s) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (row < p.n_q) v = *(const u32x4*)(Qg + (int64_t)row * p.q_sr + s * 16 + hi * 8);
       qf[qi][s] = p.neg ? flip_signs(v) : v;
     }
   }
 
-  f32x16 o[QB][2];
+  f32x16 o[QB][NDB];
   float m[QB], l[QB], mc[QB];
 #pragma unroll
   for (int qi = 0; qi < QB; ++qi) {
-    o[qi][0] = f32x16{};
-    o[qi][1] = f32x16{};
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[qi][db] = f32x16{};
     m[qi] = -INFINITY;
     l[qi] = 0.f;
     mc[qi] = 0.f;
@@ -156,25 +180,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
   const float c = p.c;
 
   // ---- staging.  K and V go straight from memory into LDS (buffer loads
-  // with an LDS destination: each wave instruction fills 1 KB = 8 keys, lane
-  // i writing bytes [16i, 16i + 16)); every lane fetches the 16-byte chunk
-  // that the permuted layout puts at its position.
-  // Piece r (= wave·CPW + i, 8 keys) of a tile: lane -> key 8r + lane / 8,
-  // LDS chunk lane % 8.  The K chunk permutation depends on the key through
-  // bits 1..3 = (4r + lane / 16) & 7, i.e. on the parity of r (CPW is even);
-  // the V one through bit 1 = (lane / 16) & 1 only.
-  uint32_t k_lane[2];
+  // with an LDS destination: each wave instruction fills 1 KB = KPP keys,
+  // lane i writing bytes [16i, 16i + 16)); every lane fetches the 16-byte
+  // chunk that the permuted layout puts at its position.
+  // Piece r (= wave·CPW + i) of a tile: lane -> key KPP·r + lane / CR, LDS
+  // chunk lane % CR.  The K permutation of that key is (4r + lane / 16) &
+  // (CR − 1), so it depends on r only through r mod NKL (and CPW is a
+  // multiple of NKL); the V one depends on lane / 16 only.
+  uint32_t k_lane[NKL];
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
-    k_lane[par] = (uint32_t)(((lane >> 3) * p.k_sr + ((lane & 7) ^ ((4 * par + (lane >> 4)) & 7)) * 8) * 2);
+  for (int v = 0; v < NKL; ++v) {
+    const int key = KPP * v + lane / CR;  // a key of a piece r ≡ v (mod NKL)
+    k_lane[v] = (uint32_t)(((lane / CR) * p.k_sr + ((lane % CR) ^ kswz<D>(key)) * 8) * 2);
+  }
   const uint32_t v_lane =
-      (uint32_t)(((lane >> 3) * p.v_sr + ((lane & 7) ^ (((lane >> 4) & 1) << 2)) * 8) * 2);
+      (uint32_t)(((lane / CR) * p.v_sr + ((lane % CR) ^ vswz<D>(lane / CR)) * 8) * 2);
   const uint32_t k_tile = (uint32_t)(BN * p.k_sr * 2), v_tile = (uint32_t)(BN * p.v_sr * 2);
+  // with fewer pieces than waves (D = 16, four waves) the last waves load none
+  const bool loader = PIECES >= NW || wave < PIECES;
 
   // issue this wave's two LDS-destination loads of K (or V) for one tile.
   // The K and V halves are issued at different points of a step, so that
   // the waves of a compute unit do not all queue their loads at once.
   auto gload_k = [&](int tile, int stage) {
+    if (!loader) return;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int r = wave * CPW + i;
@@ -182,21 +211,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
       load_lds_b128(krs,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
                         __attribute__((address_space(3))) void*)&Ks[stage][r * 512]),
-                    k_lane[i & 1] + (uint32_t)(r * 8 * p.k_sr * 2) + tile * k_tile);
+                    k_lane[i % NKL] + (uint32_t)(r * KPP * p.k_sr * 2) + tile * k_tile);
     }
   };
   auto gload_v = [&](int tile, int stage) {
+    if (!loader) return;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int r = wave * CPW + i;
       load_lds_b128(vrs,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
                         __attribute__((address_space(3))) void*)&Vs[stage][r * 512]),
-                    v_lane + (uint32_t)(r * 8 * p.v_sr * 2) + tile * v_tile);
+                    v_lane + (uint32_t)(r * KPP * p.v_sr * 2) + tile * v_tile);
     }
   };
   // K fragment (kb, st) of this lane: key kb·32 + l32, chunk 2·st + hi
-  const int kx = (l32 >> 1) & 7;
+  // (kb·32 is a multiple of 128 / D, so the permutation is that of l32)
+  const int kx = kswz<D>(l32);
   auto kfrag = [&](int buf, int kb, int st) {
     return *(const u32x4*)&Ks[buf][(kb * 32 + l32) * D + (((2 * st + hi) ^ kx) * 8)];
   };
@@ -205,11 +236,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
   // of 16-key step kb·32 + t2·16.  Two transposing reads, 4 keys each: lane
   // i of a 16-lane group points at key (i / 4) of the 4 and at d columns
   // 4·(i % 4) .. +3 of its 16; the read hands lane r element r % 4 of lane
-  // 4j + r / 4, i.e. key j at column r.
+  // 4j + r / 4, i.e. key j at column r.  With D = 16 the lanes of columns
+  // 16..31 (which do not exist) read the other four keys of the 8-key group
+  // instead, so their phase still covers distinct banks; the Oᵀ rows they
+  // produce are never stored.
   const int i16 = lane & 15;
-  const int v_key_l = 4 * hi + (i16 >> 2);          // key offset within a 16-key step (+ 8·e)
-  const int v_x = ((v_key_l >> 1) & 1) << 2;         // the row permutation (bit 1 of the key)
-  const int v_col = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);  // d within the 32-column block
+  const bool v_pad = D < 32 && ((lane >> 4) & 1);
+  const int v_key_l = (4 * hi + (i16 >> 2)) ^ (v_pad ? 4 : 0);  // key offset within a 16-key step (+ 8·e)
+  const int v_x = vswz<D>(v_key_l);  // the row permutation (the step starts at a multiple of 8)
+  const int v_col = (D < 32 ? 0 : 16 * ((lane >> 4) & 1)) + 4 * (i16 & 3);  // d within the 32-column block
   auto vfrag = [&](int buf, int kb, int t2, int db) {
     u32x4 r;
 #pragma unroll
@@ -277,7 +312,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
   auto scores = [&](auto masked, int qi, int buf, int kbase, int kb) {
     f32x16 sv = {};
 #pragma unroll
-    for (int st = 0; st < 4; ++st) sv = mfma_32x32x16<DT>(kfrag(buf, kb, st), qf[qi][st], sv);
+    for (int st = 0; st < NST; ++st) sv = mfma_32x32x16<DT>(kfrag(buf, kb, st), qf[qi][st], sv);
     if constexpr (decltype(masked)::value) apply_mask(qi, kbase, kb, sv);
     return sv;
   };
@@ -304,10 +339,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
       mc[qi] = (m_new == -INFINITY ? 0.f : m_new) * c;
       l[qi] *= alpha;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        o[qi][0][i] *= alpha;
-        o[qi][1][i] *= alpha;
-      }
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[qi][db][i] *= alpha;
       rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) rs += weights(qi, kb, scores(masked, qi, buf, kbase, kb), pw[kb]);
@@ -322,22 +356,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
   //   P0·V (MFMA) interleaved with the weights of block 1, then P1·V.
   auto tile = [&](auto masked, int buf, int kbase, auto&& mid) {
     constexpr bool MASKED = decltype(masked)::value;
-    u32x4 kf[2][4];
+    u32x4 kf[2][NST];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int st = 0; st < 4; ++st) kf[kb][st] = kfrag(buf, kb, st);
+      for (int st = 0; st < NST; ++st) kf[kb][st] = kfrag(buf, kb, st);
     f32x16 s0[2], s1[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
+      for (int st = 0; st < NST; ++st)
         s0[kb] = mfma_32x32x16<DT>(kf[kb][st], qf[0][st], st == 0 ? f32x16{} : s0[kb]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
+      for (int st = 0; st < NST; ++st)
         s1[kb] = mfma_32x32x16<DT>(kf[kb][st], qf[1][st], st == 0 ? f32x16{} : s1[kb]);
     if constexpr (MASKED) {
       apply_mask(0, kbase, 0, s0[0]);
@@ -346,17 +380,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
     uint32_t p0[2][8], p1[2][8];
     const float rs0 = weights(0, 0, s0[0], p0[0]) + weights(0, 1, s0[1], p0[1]);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 14, 0);  // then VALU / transcendental
+    for (int g = 0; g < 2 * NST; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // one MFMA of S1
+      __builtin_amdgcn_sched_group_barrier(0x402, 112 / (2 * NST), 0);  // then VALU / transcendental
     }
-    u32x4 vf[2][2][2];
+    u32x4 vf[2][2][NDB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int db = 0; db < NDB; ++db)
           vf[kb][t2][db] = vfrag(buf, kb, t2, db);
     settle(masked, 0, buf, kbase, p0, rs0);
     mid();
@@ -367,7 +401,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
+        for (int db = 0; db < NDB; ++db) {
           const u32x4 bv = {p0[kb][4 * t2], p0[kb][4 * t2 + 1], p0[kb][4 * t2 + 2], p0[kb][4 * t2 + 3]};
           o[0][db] = mfma_32x32x16<DT>(vf[kb][t2][db], bv, o[0][db]);
         }
@@ -377,9 +411,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
     }
     const float rs1 = weights(1, 0, s1[0], p1[0]) + weights(1, 1, s1[1], p1[1]);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 14, 0);
+    for (int g = 0; g < 4 * NDB; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA of P0·V
+      __builtin_amdgcn_sched_group_barrier(0x402, 112 / (4 * NDB), 0);
     }
     settle(masked, 1, buf, kbase, p1, rs1);
 
@@ -388,7 +422,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
+        for (int db = 0; db < NDB; ++db) {
           const u32x4 bv = {p1[kb][4 * t2], p1[kb][4 * t2 + 1], p1[kb][4 * t2 + 2], p1[kb][4 * t2 + 3]};
           o[1][db] = mfma_32x32x16<DT>(vf[kb][t2][db], bv, o[1][db]);
         }
@@ -402,13 +436,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s1[kb] = scores(std::false_type{}, 1, buf, kbase, kb);
     mid();
-    u32x4 vf[2][2][2];
+    u32x4 vf[2][2][NDB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int db = 0; db < NDB; ++db)
           vf[kb][t2][db] = vfrag(buf, kb, t2, db);
     if constexpr (MASKED) {
       apply_mask(1, kbase, 0, s1[0]);
@@ -422,7 +456,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
+        for (int db = 0; db < NDB; ++db) {
           const u32x4 bv = {p1[kb][4 * t2], p1[kb][4 * t2 + 1], p1[kb][4 * t2 + 2], p1[kb][4 * t2 + 3]};
           o[1][db] = mfma_32x32x16<DT>(vf[kb][t2][db], bv, o[1][db]);
         }
@@ -498,10 +532,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 1
     if (wave_active && row < p.n_q) {
       uint16_t* orow = Og + (int64_t)row * p.o_sr;
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d = db * 32 + g * 8 + hi * 4;
+          if (d >= D) continue;  // D = 16: the padding rows of Oᵀ
           const u32x2 w = {pack2<DT>(o[qi][db][4 * g] * inv, o[qi][db][4 * g + 1] * inv),
                            pack2<DT>(o[qi][db][4 * g + 2] * inv, o[qi][db][4 * g + 3] * inv)};
           *(u32x2*)(orow + d) = w;
@@ -602,22 +637,38 @@ int waves_per_wg(int64_t n_q, int64_t heads, bool /*causal*/) {
   return ((n_q + 255) / 256) * heads >= 512 ? 4 : 2;
 }
 
-template <int DT, bool CAUSAL, int NW>
+template <int DT, int DH, bool CAUSAL, int NW>
 hipError_t launch_nw(const SdpaArgs& a, hipStream_t st) {
   // causal: one wave per pair of 32-row blocks (see the kernel)
   const int64_t units = ((a.n_q + 31) / 32 + 1) / 2;
   const int64_t nqb = CAUSAL ? (units + NW - 1) / NW : (a.n_q + NW * 64 - 1) / (NW * 64);
   const int64_t grid = nqb * a.B * a.H;
-  hipLaunchKernelGGL((sdpa_fwd_kernel<DT, CAUSAL, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((sdpa_fwd_kernel<DT, DH, CAUSAL, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
-template <int DT, bool CAUSAL>
+template <int DT, int DH, bool CAUSAL>
 hipError_t launch_mfma(const SdpaArgs& a, hipStream_t st) {
   switch (waves_per_wg(a.n_q, (int64_t)a.B * a.H, CAUSAL)) {
-    case 1: return launch_nw<DT, CAUSAL, 1>(a, st);
-    case 2: return launch_nw<DT, CAUSAL, 2>(a, st);
-    default: return launch_nw<DT, CAUSAL, 4>(a, st);
+    case 1: return launch_nw<DT, DH, CAUSAL, 1>(a, st);
+    case 2: return launch_nw<DT, DH, CAUSAL, 2>(a, st);
+    default: return launch_nw<DT, DH, CAUSAL, 4>(a, st);
+  }
+}
+
+template <int DT, int DH>
+hipError_t launch_mask(const SdpaArgs& a, int causal, hipStream_t st) {
+  return causal ? launch_mfma<DT, DH, true>(a, st) : launch_mfma<DT, DH, false>(a, st);
+}
+
+template <int DT>
+hipError_t launch_dim(const SdpaArgs& a, int causal, int d, hipStream_t st) {
+  switch (d) {
+    case 16: return launch_mask<DT, 16>(a, causal, st);
+    case 32: return launch_mask<DT, 32>(a, causal, st);
+    case 64: return launch_mask<DT, 64>(a, causal, st);
+    case 128: return launch_mask<DT, 128>(a, causal, st);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -644,10 +695,7 @@ hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float sc
       default: return hipErrorInvalidValue;
     }
   }
-  if (d != D) return hipErrorInvalidValue;
-  if (dtype == DT_BF16)
-    return causal ? launch_mfma<DT_BF16, true>(a, st) : launch_mfma<DT_BF16, false>(a, st);
-  return causal ? launch_mfma<DT_F16, true>(a, st) : launch_mfma<DT_F16, false>(a, st);
+  return dtype == DT_BF16 ? launch_dim<DT_BF16>(a, causal, d, st) : launch_dim<DT_F16>(a, causal, d, st);
 }
 
 }  // namespace mha
