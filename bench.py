@@ -9,6 +9,7 @@ the causal half that is skipped is not counted.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-seconds S]
                     [--no-cpu-baseline]
+    python bench.py --head-dims     # the head-dimension variants instead
 
 Prints one JSON line.  Only one GPU is used: there is no multi-GPU path.
 """
@@ -155,6 +156,46 @@ def other_configs(dev, stream, iters=100):
     return res
 
 
+# Table 3 row (A) of the nickwang.xyz page: d_model fixed at 512, h and
+# d_k = d_v = d_model / h varied (the FLOPs stay the same); plus d_k 128 at
+# d_model 1024 (row (C)).
+HEAD_DIM_VARIANTS = ((8, 64), (32, 16), (16, 32), (4, 128), (8, 128))
+
+
+def head_dim_sweep(dev, stream, B=4, n=4096, iters=50, settle_s=1.0):
+    """mha_sdpa TFLOP/s for each head-dimension variant at [B, h, n, d],
+    both masks, scale 1/sqrt(d).  Rates use algorithmic flops."""
+    import numpy as np
+    import torch
+    from transformer_head_scaled_amd import libmha, synth
+
+    res = {}
+    for h, d in HEAD_DIM_VARIANTS:
+        ins = synth.sdpa_inputs(5, B, h, n, n, d, dtype="bf16")
+        Q, K, V = (torch.from_numpy(ins[k][0].view(np.int16)).to(dev).view(torch.bfloat16)
+                   for k in "QKV")
+        O = torch.empty_like(Q)
+        entry = {"B": B, "h": h, "n": n, "d": d}
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < settle_s:
+            for _ in range(20):
+                libmha.sdpa(Q, K, V, scale=d ** -0.5, mask="none", out=O, stream=stream)
+            torch.cuda.synchronize()
+        for mk in ("none", "causal"):
+            def call():
+                libmha.sdpa(Q, K, V, scale=d ** -0.5, mask=mk, out=O, stream=stream)
+            for _ in range(5):
+                call()
+            med, mn = time_calls(call, stream, iters)
+            fl = sdpa_flops(B, h, n, n, d, mk == "causal")
+            entry[mk] = {"us_median": round(med, 2), "us_min": round(mn, 2),
+                         "tflops": round(fl / (med * 1e-6) / 1e12, 1),
+                         "pct_peak": round(100 * fl / (med * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        res[f"h{h}_d{d}"] = entry
+        del Q, K, V, O
+    return res
+
+
 def cpu_baseline(ins, budget_s=12.0):
     """The fp64 oracle, untuned, on a bounded sample of the same workload:
     whole (batch, head) pairs, alternating unmasked and causal, until the
@@ -197,6 +238,8 @@ def main():
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the timings of the smaller workloads (reported under other_configs)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--head-dims", action="store_true",
+                    help="only time the head-dimension variants (d_k 16/32/64/128) of mha_sdpa")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -218,6 +261,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+        return 0
+    if args.head_dims:
+        out = {"head_dim_variants": head_dim_sweep(dev, torch.cuda.current_stream()),
+               "dtype": "bf16", "data": "synthetic", "unit": "TFLOP/s"}
+        print(json.dumps(out), flush=True)
         return 0
     w = WORKLOAD
     B, h, n, d = w["B"], w["h"], w["n"], w["d"]
@@ -309,10 +357,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(ach_nc, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach_nc / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "sdpa_fwd_kernel<bf16, non-causal, 4 waves>"},
+                     "kernel": "sdpa_fwd_kernel<bf16, d 64, non-causal, 4 waves>"},
         "roofline_causal": {"bound": "mfma", "achieved": round(ach_c, 2), "peak": PEAK_BF16_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(ach_c / PEAK_BF16_TFLOPS, 4),
-                            "kernel": "sdpa_fwd_kernel<bf16, causal, 4 waves>"},
+                            "kernel": "sdpa_fwd_kernel<bf16, d 64, causal, 4 waves>"},
     }
     if not args.no_other_configs:
         res["other_configs"] = other_configs(dev, stream)
