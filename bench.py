@@ -95,7 +95,11 @@ def other_configs(dev, stream, iters=100):
     working set fits the 256 MB last-level cache): mha_forward self
     attention with key padding (B 32, n 64, d_model 512, h 8), causal SDPA
     (B 16, h 8, n 512), mha_forward cross attention (B 8, n_q 384, n_k 512,
-    d_model 1024, h 16).  Rates use algorithmic flops and bytes."""
+    d_model 1024, h 16), and one decoding step (B 64, h 8, one query row
+    against a 2048-entry key/value cache, HBM-bound).  Rates use algorithmic
+    flops and bytes.  Cold calls follow a read of a 512 MB buffer (a read
+    leaves clean lines; an overwrite would leave dirty ones that the timed
+    call then writes back)."""
     import numpy as np
     import torch
     from transformer_head_scaled_amd import libmha, synth
@@ -103,10 +107,10 @@ def other_configs(dev, stream, iters=100):
     def dev_t(st):
         return torch.from_numpy(np.ascontiguousarray(st).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MB
 
     def flush():
-        scratch.fill_(1)
+        scratch.sum()
 
     res = {}
     for cfg in (2, 4):
@@ -152,6 +156,26 @@ def other_configs(dev, stream, iters=100):
                       "gbs_cold": round(nbytes / (cmed * 1e-6) / 1e9, 1),
                       "hbm_frac_cold": round(nbytes / (cmed * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                       "flops": fl, "bytes": nbytes}
+    # decoding step: bytes = the visible K and V rows + Q + O
+    w = synth.WORKLOADS[6]
+    ins, lens = synth.workload_inputs(6)
+    Qd, Kd, Vd = (dev_t(ins[k][0]) for k in "QKV")
+    Od = torch.empty_like(Qd)
+    lens_d = torch.from_numpy(lens).to(dev)
+
+    def call6():
+        libmha.sdpa(Qd, Kd, Vd, scale=0.125, mask="none", seq_lens=lens_d, out=Od, stream=stream)
+    for _ in range(20):
+        call6()
+    med, mn = time_calls(call6, stream, iters)
+    cmed, _ = time_calls(call6, stream, max(iters // 4, 10), flush)
+    nbytes = w["h"] * int(lens.sum()) * w["d"] * 2 * 2 + 2 * w["B"] * w["h"] * w["n_q"] * w["d"] * 2
+    res[w["name"]] = {"call": "mha_sdpa (key split)", "us_median": round(med, 2), "us_min": round(mn, 2),
+                      "us_median_cold": round(cmed, 2),
+                      "gbs": round(nbytes / (med * 1e-6) / 1e9, 1),
+                      "gbs_cold": round(nbytes / (cmed * 1e-6) / 1e9, 1),
+                      "hbm_frac_cold": round(nbytes / (cmed * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                      "bytes": nbytes}
     del scratch
     return res
 

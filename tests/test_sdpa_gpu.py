@@ -187,6 +187,45 @@ def test_head_dims_four_wave(d, mask):
         _check(got[b, i], exp, "bf16", f"d={d} {mask} head ({b},{i}) len {lens[b]}")
 
 
+# Decoding steps (a few new query positions against the cached keys and
+# values of a sequence, as in beam-search inference): the four waves of a
+# workgroup split the key range and merge their partial results.  Key
+# lengths leave some waves without any tile (0, 1, 64, 65), give ragged
+# last tiles, and run past n_k; one and two 32-row query blocks.
+DECODE_CASES = [
+    # (B, h, n_q, n_k, lens)
+    (8, 4, 1, 2048, [2048, 1, 0, 64, 65, 300, 1999, 5000]),
+    (4, 2, 4, 1000, [1000, 513, 256, 3]),
+    (3, 2, 33, 512, None),
+    (2, 3, 64, 777, [777, 700]),
+]
+
+
+def test_workload_decode_step():
+    """The decoding-step workload (64 beams, h 8, one query row against a
+    2048-entry cache with lengths in [1792, 2048]), all outputs."""
+    w = synth.WORKLOADS[6]
+    ins, lens = synth.workload_inputs(6)
+    note("sdpa bf16 decode workload [64,8,1,2048]")
+    got = _run(ins, "bf16", "none", lens)
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], 0.125, oracle.MASK_NONE, lens)
+    _check(got, exp, "bf16", w["name"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("case", DECODE_CASES,
+                         ids=lambda c: "x".join(map(str, c[:4])) + ("_lens" if c[4] else ""))
+def test_decode_key_split(dtype, d, case):
+    B, h, n_q, n_k, lens = case
+    scale = 1 / math.sqrt(d)
+    ins = synth.sdpa_inputs(400 + d + n_q, B, h, n_q, n_k, d, dtype=dtype)
+    note(f"sdpa {dtype} decode d={d} {case}")
+    got = _run(ins, dtype, "none", lens, scale=scale)
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], scale, oracle.MASK_NONE, lens)
+    _check(got, exp, dtype, f"{dtype} decode d={d} {case}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 1.0])
 def test_unusual_scales(dtype, scale):

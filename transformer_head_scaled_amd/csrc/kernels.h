@@ -24,7 +24,7 @@ struct SdpaArgs {
 };
 
 hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float scale, hipStream_t st);
-int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t heads);
+int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t n_k, int64_t heads);
 
 // One GEMM C = A·W of the projections: A [M, K] row-major (row stride lda),
 // W [K, N] row-major (row stride ldw).  Output element (m, n) is written to

@@ -167,7 +167,7 @@ int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype
                  "rows/wg=%d flops(dense-visible)=%.4g bytes=%.4g\n",
                  (int)dtype, (long long)B, (long long)h, (long long)n_q, (long long)n_k,
                  (long long)d_k, (int)mask_kind, seq_lens ? "yes" : "no",
-                 mha::sdpa_rows_per_workgroup(dtype, mask_kind == MHA_MASK_CAUSAL, n_q, B * h), 4.0 * d_k * vis * B * h,
+                 mha::sdpa_rows_per_workgroup(dtype, mask_kind == MHA_MASK_CAUSAL, n_q, n_k, B * h), 4.0 * d_k * vis * B * h,
                  (double)es * B * h * (2 * n_q * d_k + 2 * n_k * d_k));
   }
   const hipError_t e = mha::launch_sdpa(a, dtype, mask_kind == MHA_MASK_CAUSAL, (int)d_k, scale,

@@ -84,10 +84,37 @@ __host__ __device__ constexpr int vswz(int key) {
 // NW waves per workgroup, each owning 64 query rows (two blocks of 32), for
 // head dimension DH = d_k = d_v in {16, 32, 64, 128}.  With DH = 128 the
 // accumulators need more than 256 registers, so one wave per SIMD.
-template <int DT, int DH, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 1 || DH > 64) ? 1 : 2, 2))) void sdpa_fwd_kernel(SdpaArgs p) {
+//
+// SPLIT (few query rows, long key range, no causal mask -- a decoding step
+// against a key/value cache): the NW waves of a workgroup share ONE 32-row
+// query block and split the key range instead, wave w taking tiles w, w + NW,
+// w + 2·NW, ... through a ring of its own in LDS, with no workgroup barrier
+// in the key loop; at the end the NW partial results (reference value, row
+// sum, unnormalised O) are merged through LDS with the rescale of the online
+// softmax.  NW times the loads in flight per (batch, head); the ring of a
+// wave has SPLIT_STAGES stages, so that many − 1 tiles are in flight.
+#ifndef SDPA_SPLIT_STAGES
+#define SDPA_SPLIT_STAGES 2
+#endif
+#ifndef SDPA_SPLIT_NW
+#define SDPA_SPLIT_NW 4
+#endif
+// Ring stages of the key split for head dimension d: a wave's wait leaves
+// (stages − 2) tiles of 2·(d / 8) load instructions outstanding, below the
+// counter's 64.
+constexpr int split_stages(int d) {
+  return SDPA_SPLIT_STAGES < 2 + 63 / (2 * (d / 8)) ? SDPA_SPLIT_STAGES : 2 + 63 / (2 * (d / 8));
+}
+// Waves of the key split: a ring per wave, waves × stages × 64 keys × (K + V)
+// rows of 2·d bytes within 128 KB of LDS.
+constexpr int split_waves(int d) {
+  return SDPA_SPLIT_NW < 512 / d / split_stages(d) ? SDPA_SPLIT_NW : 512 / d / split_stages(d);
+}
+template <int DT, int DH, bool CAUSAL, int NW, bool SPLIT = false>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 1 || DH > 64 || SPLIT) ? 1 : 2, 2))) void sdpa_fwd_kernel(SdpaArgs p) {
+  static_assert(!(SPLIT && CAUSAL), "the key split is for the unmasked case");
   constexpr int D = DH;
-  constexpr int QB = 2, BN = 64, NSTAGE = 2;
+  constexpr int QB = 2, BN = 64, NSTAGE = SPLIT ? split_stages(DH) : 2;
   constexpr int BM = NW * 32 * QB;  // query rows per workgroup
   constexpr int NST = D / 16;       // 16-deep MFMA steps of a score block
   constexpr int NDB = D >= 32 ? D / 32 : 1;  // 32-row blocks of Oᵀ (d = 16: one, half used)
@@ -99,12 +126,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head dimension");
   static_assert(CPW % NKL == 0, "a wave's first piece must start a K offset cycle");
   constexpr float kAccept = 256.f;  // accept a tile while partial row sums are <= 2^8
+  constexpr int NBUF = SPLIT ? NW : 1;  // LDS rings: one per wave with the key split
 
   // K tile: [key][D], rows of D / 8 16-byte chunks permuted by kswz
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[NSTAGE][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF][NSTAGE][BN * D];
   // V tile: [key][D], chunks permuted by vswz, which keeps the transposing
   // fragment reads conflict-free
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[NSTAGE][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NBUF][NSTAGE][BN * D];
 
   // Rows.  Unmasked: workgroup qb of a head takes rows [qb·BM, qb·BM + BM),
   // each wave 64 consecutive rows.  Causal: the work of a row grows with its
@@ -114,7 +142,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   // run side by side until the end, instead of a long wave finishing alone.
   const int nb32e = ((p.n_q + 31) / 32 + 1) & ~1;
   const int units = nb32e / 2;  // causal: waves of work per head
-  const int nqb = CAUSAL ? (units + NW - 1) / NW : (p.n_q + BM - 1) / BM;
+  const int nqb = SPLIT ? (p.n_q + 31) / 32 : CAUSAL ? (units + NW - 1) / NW : (p.n_q + BM - 1) / BM;
   const uint32_t total = (uint32_t)nqb * p.B * p.H;
   const uint32_t t = xcd_remap(blockIdx.x, total);
   const int bh = t / nqb;
@@ -131,6 +159,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   if (CAUSAL) {
     row0[0] = 32 * unit;
     row0[1] = 32 * (nb32e - 1 - unit);
+  } else if (SPLIT) {
+    // one block per workgroup; the tile code of the upper block does the work
+    row0[0] = row0[1] = 32 * qb;
   } else {
     row0[0] = qb * BM + wave * 64;
     row0[1] = row0[0] + 32;
@@ -197,7 +228,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
       (uint32_t)(((lane / CR) * p.v_sr + ((lane % CR) ^ vswz<D>(lane / CR)) * 8) * 2);
   const uint32_t k_tile = (uint32_t)(BN * p.k_sr * 2), v_tile = (uint32_t)(BN * p.v_sr * 2);
   // with fewer pieces than waves (D = 16, four waves) the last waves load none
-  const bool loader = PIECES >= NW || wave < PIECES;
+  const bool loader = SPLIT || PIECES >= NW || wave < PIECES;
+  constexpr int LPW = SPLIT ? PIECES : CPW;  // pieces this wave loads per tile
+  const int kvw = SPLIT ? wave : 0;          // this wave's LDS ring
 
   // issue this wave's two LDS-destination loads of K (or V) for one tile.
   // The K and V halves are issued at different points of a step, so that
@@ -205,23 +238,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   auto gload_k = [&](int tile, int stage) {
     if (!loader) return;
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int r = wave * CPW + i;
+    for (int i = 0; i < LPW; ++i) {
+      const int r = (SPLIT ? 0 : wave * CPW) + i;
       // (the destinations are per wave: readfirstlane makes them scalars)
       load_lds_b128(krs,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-                        __attribute__((address_space(3))) void*)&Ks[stage][r * 512]),
+                        __attribute__((address_space(3))) void*)&Ks[kvw][stage][r * 512]),
                     k_lane[i % NKL] + (uint32_t)(r * KPP * p.k_sr * 2) + tile * k_tile);
     }
   };
   auto gload_v = [&](int tile, int stage) {
     if (!loader) return;
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int r = wave * CPW + i;
+    for (int i = 0; i < LPW; ++i) {
+      const int r = (SPLIT ? 0 : wave * CPW) + i;
       load_lds_b128(vrs,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-                        __attribute__((address_space(3))) void*)&Vs[stage][r * 512]),
+                        __attribute__((address_space(3))) void*)&Vs[kvw][stage][r * 512]),
                     v_lane + (uint32_t)(r * KPP * p.v_sr * 2) + tile * v_tile);
     }
   };
@@ -229,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   // (kb·32 is a multiple of 128 / D, so the permutation is that of l32)
   const int kx = kswz<D>(l32);
   auto kfrag = [&](int buf, int kb, int st) {
-    return *(const u32x4*)&Ks[buf][(kb * 32 + l32) * D + (((2 * st + hi) ^ kx) * 8)];
+    return *(const u32x4*)&Ks[kvw][buf][(kb * 32 + l32) * D + (((2 * st + hi) ^ kx) * 8)];
   };
   // Vᵀ fragment (kb, t2, db): d = db·32 + l32 and the 8 keys that the score
   // registers hold for this lane half, {4·hi .. 4·hi+3, 8+4·hi .. 8+4·hi+3}
@@ -252,7 +285,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
       const int key = kb * 32 + t2 * 16 + 8 * e + v_key_l;
       const int d = db * 32 + v_col;
       const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)&Vs[buf][key * D + (((d >> 3) ^ v_x) * 8) + (d & 7)]);
+          (lds_s16x4*)&Vs[kvw][buf][key * D + (((d >> 3) ^ v_x) * 8) + (d & 7)]);
       const u32x2 w = __builtin_bit_cast(u32x2, v);
       r[2 * e] = w[0];
       r[2 * e + 1] = w[1];
@@ -260,16 +293,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
     return r;
   };
 
+  // tiles this wave takes with the key split (j = wave + t·NW)
+  const int myn = SPLIT ? (ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0) : 0;
+  // vmcnt that leaves the loads of KEEP later tiles outstanding (each tile is
+  // 2·LPW load instructions of this wave)
+  constexpr int kSplitKeep = SPLIT ? (NSTAGE - 2) * 2 * LPW : 0;
+  static_assert(kSplitKeep < 64, "vmcnt range");
+  constexpr int kSplitWait = (kSplitKeep & 15) | ((kSplitKeep >> 4) << 14) | 0x0070;
+  if (SPLIT) {
 #pragma unroll
-  for (int t0 = 0; t0 < NSTAGE - 1; ++t0)
-    if (t0 < ntiles) {
-      gload_k(t0, t0);
-      gload_v(t0, t0);
-    }
+    for (int t0 = 0; t0 < NSTAGE - 1; ++t0)  // this wave's first tiles
+      if (t0 < myn) {
+        gload_k(wave + t0 * NW, t0);
+        gload_v(wave + t0 * NW, t0);
+      }
+  } else {
+#pragma unroll
+    for (int t0 = 0; t0 < NSTAGE - 1; ++t0)
+      if (t0 < ntiles) {
+        gload_k(t0, t0);
+        gload_v(t0, t0);
+      }
+  }
   // tile 0 has landed (at most the four loads of tile 1 are outstanding),
   // then the workgroup barrier; the "memory" clobber keeps LDS accesses on
   // their side of it
-  if (NSTAGE > 2 && ntiles > 1)
+  if (SPLIT && myn >= NSTAGE - 1)
+    __builtin_amdgcn_s_waitcnt(kSplitWait);  // tile 0 landed, the later ones may be out
+  else if (!SPLIT && NSTAGE > 2 && ntiles > 1)
     __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
   else
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
@@ -496,7 +547,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   using yes = std::true_type;
   const int nfull = min(n_eff / BN, ntiles);  // tiles inside the valid keys
   int j = 0;
-  if (!CAUSAL) {
+  if (SPLIT) {
+    // this wave's tiles j = wave + t·NW through its own ring: the loads of
+    // tile t + NSTAGE − 1 go out at the top of step t (K) and mid-tile (V)
+    // into the stage that step t − 1 read; the step ends with this wave's
+    // own wait for tile t + 1 (no barrier)
+    auto split_step = [&](int t, auto masked) {
+      const int jt = wave + t * NW;
+      const int ta = t + NSTAGE - 1;
+      const bool more = ta < myn;
+      if (more) gload_k(wave + ta * NW, ta % NSTAGE);
+      auto load_v = [&]() {
+        if (more) gload_v(wave + ta * NW, ta % NSTAGE);
+      };
+      tile_hi(masked, t % NSTAGE, jt * BN, load_v);
+      if (more)
+        __builtin_amdgcn_s_waitcnt(kSplitWait);  // tiles t + 2 .. ta may be out
+      else
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    };
+    int t = 0;
+    for (; wave + t * NW < nfull; ++t) split_step(t, no{});
+    for (; wave + t * NW < ntiles; ++t) split_step(t, yes{});
+  } else if (!CAUSAL) {
     for (; j < nfull; ++j) step(j, no{}, std::integral_constant<int, 2>{});
     for (; j < ntiles; ++j) step(j, yes{}, std::integral_constant<int, 2>{});
   } else {
@@ -523,9 +596,48 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
     for (; j < ntiles; ++j) step(j, no{}, std::integral_constant<int, 0>{});
   }
 
+  if constexpr (SPLIT) {
+    // Merge the NW partial results of the block.  Every wave is past its last
+    // LDS access (its own wait) once the barrier passes, so the rings hold the
+    // exchange, lane-contiguous: per wave 16·NDB output values in the V
+    // rings, reference value and row sum in the K rings.
+    constexpr int NO = 16 * NDB;
+    static_assert(NW * NO * 64 * 4 <= (int)sizeof(Vs) && NW * 2 * 64 * 4 <= (int)sizeof(Ks),
+                  "exchange area");
+    float* xo = (float*)&Vs[0][0][0];
+    float* xm = (float*)&Ks[0][0][0];
+    asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xo[((wave * NO) + 16 * db + i) * 64 + lane] = o[1][db][i];
+    // a wave that had no tile has no reference value
+    xm[(wave * 2) * 64 + lane] = m[1] == -INFINITY ? -INFINITY : mc[1];
+    xm[(wave * 2 + 1) * 64 + lane] = l[1];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    if (wave != 0) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, xm[(w * 2) * 64 + lane]);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[1][db] = f32x16{};
+    l[1] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = xm[(w * 2) * 64 + lane];
+      const float sw = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      l[1] += sw * xm[(w * 2 + 1) * 64 + lane];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[1][db][i] += sw * xo[((w * NO) + 16 * db + i) * 64 + lane];
+    }
+  }
+
   // ---- normalise and store this lane's query row (4 consecutive d per store)
 #pragma unroll
-  for (int qi = 0; qi < QB; ++qi) {
+  for (int qi = SPLIT ? 1 : 0; qi < QB; ++qi) {
     const float L = pair_sum(l[qi]);
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const int row = row0[qi] + l32;
@@ -637,6 +749,28 @@ int waves_per_wg(int64_t n_q, int64_t heads, bool /*causal*/) {
   return ((n_q + 255) / 256) * heads >= 512 ? 4 : 2;
 }
 
+template <int DT, int DH, int NW>
+hipError_t launch_split(const SdpaArgs& a, hipStream_t st) {
+  const int64_t grid = (a.n_q + 31) / 32 * a.B * a.H;
+  hipLaunchKernelGGL((sdpa_fwd_kernel<DT, DH, false, NW, true>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+// The key split: few query rows (one or two 32-row blocks) against a long
+// key range (at least two key tiles per wave), unmasked, and too few
+// (batch, head) pairs for one-wave workgroups to keep enough loads in
+// flight (measured: with 2048 pairs and 512 keys the unsplit launch, which
+// fits several workgroups per CU, is faster).
+#ifndef SDPA_SPLIT_MIN_NK
+#define SDPA_SPLIT_MIN_NK 512
+#endif
+#ifndef SDPA_SPLIT_MAX_HEADS
+#define SDPA_SPLIT_MAX_HEADS 1024
+#endif
+bool use_split(int64_t n_q, int64_t n_k, int64_t heads, bool causal) {
+  return !causal && n_q <= 64 && n_k >= SDPA_SPLIT_MIN_NK && heads < SDPA_SPLIT_MAX_HEADS;
+}
+
 template <int DT, int DH, bool CAUSAL, int NW>
 hipError_t launch_nw(const SdpaArgs& a, hipStream_t st) {
   // causal: one wave per pair of 32-row blocks (see the kernel)
@@ -649,6 +783,8 @@ hipError_t launch_nw(const SdpaArgs& a, hipStream_t st) {
 
 template <int DT, int DH, bool CAUSAL>
 hipError_t launch_mfma(const SdpaArgs& a, hipStream_t st) {
+  if (use_split(a.n_q, a.n_k, (int64_t)a.B * a.H, CAUSAL))
+    return launch_split<DT, DH, split_waves(DH)>(a, st);
   switch (waves_per_wg(a.n_q, (int64_t)a.B * a.H, CAUSAL)) {
     case 1: return launch_nw<DT, DH, CAUSAL, 1>(a, st);
     case 2: return launch_nw<DT, DH, CAUSAL, 2>(a, st);
@@ -681,8 +817,10 @@ hipError_t launch_f32(const SdpaArgs& a, float scale, int causal, hipStream_t st
 
 }  // namespace
 
-int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t heads) {
-  return dtype == DT_F32 ? 64 : waves_per_wg(n_q, heads, causal != 0) * 64;
+int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t n_k, int64_t heads) {
+  if (dtype == DT_F32) return 64;
+  if (use_split(n_q, n_k, heads, causal != 0)) return 32;
+  return waves_per_wg(n_q, heads, causal != 0) * 64;
 }
 
 hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float scale, hipStream_t st) {

@@ -25,8 +25,12 @@ T_XQ, T_XKV, T_WQ, T_WK, T_WV, T_WO, T_LENS = 0, 1, 2, 3, 4, 5, 6
 
 DTYPES = ("f32", "bf16", "f16")
 
-# The five workloads: sizes only.  "sdpa" workloads feed Q/K/V directly;
-# "mha" workloads feed x_q, x_kv and the four weights.
+# The workloads: sizes only.  "sdpa" workloads feed Q/K/V directly; "mha"
+# workloads feed x_q, x_kv and the four weights.  1-5 are the sublayer's
+# configurations; 6 is one decoding step of the base model (beam search with
+# 4 beams over 16 sequences, [N] §6.1: each beam's new position attends to
+# its cached keys and values; caches of similar length, as in
+# length-bucketed batches).
 WORKLOADS = {
     1: dict(name="sdpa_f32_b1_h1_n16_d64", kind="sdpa", dtype="f32", B=1, h=1,
             n_q=16, n_k=16, d=64, masks=("none",), lens=None),
@@ -42,6 +46,8 @@ WORKLOADS = {
     5: dict(name="sdpa_bf16_b4_h8_n4096_d64", kind="sdpa", dtype="bf16", B=4,
             h=8, n_q=4096, n_k=4096, d=64, masks=("none", "causal"),
             lens=None),
+    6: dict(name="sdpa_decode_bf16_b64_h8_nq1_nk2048_cache", kind="sdpa", dtype="bf16",
+            B=64, h=8, n_q=1, n_k=2048, d=64, masks=("none",), lens=(1792, 2048)),
 }
 
 
