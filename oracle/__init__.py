@@ -21,6 +21,10 @@ title and section:
 * ml-canon.vercel.app, "32 Transformer" -- "PyTorch: реализация" (the
   (..., seq, d_k) layout, the head split by columns, weights multiplied on
   the right).
+* nickwang.xyz, the section on the encoder and decoder stacks (paper §3.1):
+  the residual connection and layer normalisation around each sub-layer,
+  LayerNorm(x + Sublayer(x)) (``layernorm.py``; LayerNorm itself is the
+  standard definition, which the pages do not write out).
 
 Parity status: every public function is pinned by tests under ``tests/``
 (``test_oracle_pins.py`` and ``test_oracle_mutants.py``); none is "parity
@@ -41,3 +45,4 @@ from .attention import (  # noqa: F401
     visible,
     weighted_sum,
 )
+from .layernorm import add_norm, layer_norm, mha_add_norm  # noqa: F401

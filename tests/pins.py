@@ -11,6 +11,7 @@ where the inputs are first rounded to the device dtype.
 Implementation signatures:
   sdpa_fn(Q, K, V, scale, mask_kind, seq_lens) -> ndarray [B, h, n_q, d_v]
   mha_fn(x_q, x_kv, Wq, Wk, Wv, Wo, h, mask_kind, kv_lens) -> [B, n_q, d_model]
+  add_norm_fn(x, sub, gamma, beta, eps) -> [rows, d]   (LayerNorm(x + sub))
 Inputs are float64 numpy arrays; an implementation that stores lower
 precision rounds them itself, and ``rnd`` (a function array -> array) lets a
 pin build its expected value from the rounded inputs.
@@ -399,3 +400,77 @@ def pin_mha_single_head(mha_fn, sdpa_fn, atol=1e-10):
 
 MHA_PINS = [pin_mha_shapes, pin_mha_head_blocks, pin_mha_head_permutation,
             pin_mha_single_head]
+
+
+# ---- Add & Norm ([N], the section on the encoder and decoder stacks, paper
+# §3.1): a sub-layer's output is LayerNorm(x + Sublayer(x)).  LayerNorm is
+# not written out on the pages; the pins fix the standard per-position
+# normalisation through values and properties, not through its formula.
+# Inputs are multiples of 1/8 below 32 in magnitude, exact in bf16, fp16 and
+# fp32, so every pin holds for a device implementation as it stands.
+
+def _eighths(rs, *shape, scale=8):
+    return np.round(rs.standard_normal(shape) * scale) / 8.0
+
+
+def pin_ln_hand_values(add_norm_fn, atol=1e-12):
+    """Rows whose mean and mean squared deviation are known by inspection."""
+    d = 64
+    g, b = np.ones(d), np.zeros(d)
+    pm = np.tile([-1.0, 1.0], d // 2)[None]             # mean 0, mean square 1
+    z4 = np.tile([0.0, 0.0, 0.0, 4.0], d // 4)[None]     # mean 1, deviations -1,-1,-1,3: mean square 3
+    zero = np.zeros((1, d))
+    _close(add_norm_fn(pm, zero, g, b, 0.0), pm, atol, "±1 row, eps 0")
+    # eps sits under the square root: variance 1 + eps 1 -> 1/√2
+    _close(add_norm_fn(pm, zero, g, b, 1.0), pm / math.sqrt(2.0), atol, "±1 row, eps 1")
+    exp4 = np.tile([-1.0, -1.0, -1.0, 3.0], d // 4)[None] / math.sqrt(3.0)
+    _close(add_norm_fn(z4, zero, g, b, 0.0), exp4, atol, "0,0,0,4 row")
+    # the residual addition: x and sub add up to the same row
+    _close(add_norm_fn(z4 - pm, pm, g, b, 0.0), exp4, atol, "row split over x and sub")
+
+
+def pin_ln_moments(add_norm_fn, atol=1e-12, rows=6, d=128):
+    """With gain 1, bias 0, eps 0 every output row has mean 0 and mean
+    square 1 -- per row (position), whatever the row's own mean and spread."""
+    rs = np.random.RandomState(11)
+    x = _eighths(rs, rows, d) + np.arange(rows)[:, None]
+    sub = _eighths(rs, rows, d) * (1 + np.arange(rows)[:, None] % 3)
+    y = np.asarray(add_norm_fn(x, sub, np.ones(d), np.zeros(d), 0.0), dtype=np.float64)
+    _close(y.mean(axis=1), np.zeros(rows), atol, "row means")
+    _close((y * y).mean(axis=1), np.ones(rows), 4 * atol, "row mean squares")
+
+
+def pin_ln_shift_and_scale(add_norm_fn, atol=1e-12, rows=4, d=64):
+    """eps 0: adding a constant to a row changes nothing; scaling it by a > 0
+    changes nothing, by -1 flips the sign of (y - beta)."""
+    rs = np.random.RandomState(12)
+    x, sub = _eighths(rs, rows, d), _eighths(rs, rows, d)
+    g, b = 1 + _eighths(rs, d, scale=2) / 4, _eighths(rs, d, scale=2)
+    y = np.asarray(add_norm_fn(x, sub, g, b, 0.0), dtype=np.float64)
+    _close(add_norm_fn(x + 4.0, sub, g, b, 0.0), y, atol, "shift by 4")
+    _close(add_norm_fn(2.0 * x, 2.0 * sub, g, b, 0.0), y, atol, "scale by 2")
+    _close(add_norm_fn(-x, -sub, g, b, 0.0), 2 * b[None] - y, atol, "scale by -1")
+
+
+def pin_ln_gain_bias(add_norm_fn, atol=1e-12, rows=3, d=64):
+    """Gain and bias act per feature after the normalisation:
+    y(g, b) = g * y(1, 0) + b."""
+    rs = np.random.RandomState(13)
+    x, sub = _eighths(rs, rows, d), _eighths(rs, rows, d)
+    g, b = _eighths(rs, d, scale=2), _eighths(rs, d, scale=2)
+    y0 = np.asarray(add_norm_fn(x, sub, np.ones(d), np.zeros(d), 1e-3), dtype=np.float64)
+    _close(add_norm_fn(x, sub, g, b, 1e-3), g[None] * y0 + b[None], atol, "gain and bias")
+
+
+def pin_ln_constant_row(add_norm_fn, atol=0.0, rows=3, d=64):
+    """x + sub constant along a row: zero deviation, so the output is the
+    bias exactly (eps > 0)."""
+    rs = np.random.RandomState(14)
+    x = _eighths(rs, rows, d)
+    b = _eighths(rs, d, scale=2)
+    y = add_norm_fn(x, 5.0 - x, _eighths(rs, d, scale=2), b, 1e-5)
+    _close(y, np.broadcast_to(b, (rows, d)), atol, "constant row")
+
+
+LN_PINS = [pin_ln_hand_values, pin_ln_moments, pin_ln_shift_and_scale, pin_ln_gain_bias,
+           pin_ln_constant_row]

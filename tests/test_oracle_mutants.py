@@ -219,3 +219,59 @@ def test_unmutated_copy_passes():
             pin(good, _sdpa)
         else:
             pin(good)
+
+
+# ---- Add & Norm mutants: copies of oracle.add_norm with one planted mistake
+
+def _add_norm_variant(mistake):
+    def add_norm(x, sub, gamma, beta, eps):
+        x, sub = np.asarray(x, float), np.asarray(sub, float)
+        gamma, beta = np.asarray(gamma, float), np.asarray(beta, float)
+        z = x if mistake == "no_residual" else x + sub
+        if mistake == "norm_before_add":
+            z = x  # normalise x alone, add sub afterwards
+        d = z.shape[-1]
+        axis = 0 if mistake == "wrong_axis" else -1
+        mu = z.mean(axis=axis, keepdims=True)
+        dev = z - mu
+        denom = d - 1 if mistake == "unbiased_variance" else d
+        var = (dev * dev).sum(axis=axis, keepdims=True) / (denom if axis == -1 else z.shape[0])
+        if mistake == "raw_second_moment":
+            var = (z * z).mean(axis=axis, keepdims=True)
+        if mistake == "eps_outside_sqrt":
+            y = dev / (np.sqrt(var) + eps)
+        else:
+            y = dev / np.sqrt(var + eps)
+        if mistake == "no_centering":
+            y = z / np.sqrt(var + eps)
+        if mistake == "gain_bias_swapped":
+            y = beta * y + gamma
+        else:
+            y = gamma * y + beta
+        if mistake == "norm_before_add":
+            y = y + sub
+        return y
+    return add_norm
+
+
+LN_MUTANTS = ["no_residual", "norm_before_add", "wrong_axis", "unbiased_variance",
+              "raw_second_moment", "eps_outside_sqrt", "no_centering", "gain_bias_swapped"]
+
+
+@pytest.mark.parametrize("name", LN_MUTANTS)
+def test_add_norm_mutant_is_caught(name):
+    mutant = _add_norm_variant(name)
+    failed = []
+    for pin in pins.LN_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mutant)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
+
+
+def test_add_norm_unmutated_copy_passes():
+    good = _add_norm_variant(None)
+    for pin in pins.LN_PINS:
+        pin(good)

@@ -184,3 +184,46 @@ def test_fully_masked_and_empty():
     assert np.all(out == 0)
     out = oracle.sdpa(Q, K, V, 0.5, oracle.MASK_NONE, [99])   # clamped to n_k
     np.testing.assert_allclose(out, oracle.sdpa(Q, K, V, 0.5), atol=0)
+
+
+# ---- Add & Norm (oracle.layernorm)
+
+@pytest.mark.parametrize("pin", pins.LN_PINS, ids=lambda p: p.__name__)
+def test_add_norm_pin(pin):
+    pin(oracle.add_norm)
+
+
+@pytest.mark.parametrize("eps", [1e-6, 1e-5, 0.5])
+def test_add_norm_torch_fp64(eps):
+    """torch.nn.functional.layer_norm on the CPU in float64 (a library
+    routine the oracle shares nothing with), applied to x + sub."""
+    import torch.nn.functional as F
+    rs = np.random.default_rng(500)
+    x = rs.standard_normal((7, 96)) * 2 + 0.5
+    sub = rs.standard_normal((7, 96))
+    g, b = rs.standard_normal(96), rs.standard_normal(96)
+    ref = F.layer_norm(torch.from_numpy(x + sub), (96,), torch.from_numpy(g), torch.from_numpy(b),
+                       eps).numpy()
+    np.testing.assert_allclose(oracle.add_norm(x, sub, g, b, eps), ref, rtol=0, atol=1e-12)
+
+
+def test_mha_add_norm_torch_fp64():
+    """The attention sub-layer with its Add & Norm against torch's own
+    routines in float64: multi_head_attention_forward (no biases, separate
+    projection weights) and layer_norm of x + its output, the post-norm
+    order."""
+    import torch.nn.functional as F
+    rs = np.random.default_rng(501)
+    B, n, d_model, h = 2, 13, 64, 4
+    x = rs.standard_normal((B, n, d_model))
+    Wq, Wk, Wv, Wo = (rs.standard_normal((d_model, d_model)) / math.sqrt(d_model) for _ in range(4))
+    g, b = rs.standard_normal(d_model), rs.standard_normal(d_model)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))  # noqa: E731
+    xt = t(x.transpose(1, 0, 2))
+    attn, _ = F.multi_head_attention_forward(
+        xt, xt, xt, d_model, h, None, None, None, None, False, 0.0, t(Wo.T), None,
+        training=False, need_weights=False, use_separate_proj_weight=True,
+        q_proj_weight=t(Wq.T), k_proj_weight=t(Wk.T), v_proj_weight=t(Wv.T))
+    ref = F.layer_norm(xt + attn, (d_model,), t(g), t(b), 1e-5).numpy().transpose(1, 0, 2)
+    got = oracle.mha_add_norm(x, None, Wq, Wk, Wv, Wo, g, b, 1e-5, h)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
