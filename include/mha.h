@@ -123,6 +123,47 @@ int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* W
 size_t mha_forward_workspace_size(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model,
                                   int32_t h, int32_t dtype);
 
+/*
+ * Residual connection and layer normalisation ("Add & Norm"), [N] the
+ * section on the encoder and decoder stacks (paper §3.1): every sub-layer's
+ * output is LayerNorm(x + Sublayer(x)), normalisation after the addition.
+ * LayerNorm (not written out on the pages; the standard definition) acts on
+ * each row of d_model features on its own:
+ *   z = x + sub,  mu = mean(z),  var = mean((z - mu)^2),
+ *   out = gamma ⊙ (z - mu) / sqrt(var + eps) + beta.
+ * Sums and normalisation in fp32, output rounded once to dtype.
+ *
+ * mha_add_norm: x, sub, out [rows, d_model] row-major, contiguous; gamma,
+ *   beta [d_model]; all of dtype (F32, BF16 or F16), device pointers,
+ *   16-byte aligned.  out may be x or sub (in place); any other overlap of
+ *   out with an input is MHA_ERR_ALIAS.  eps finite and >= 0 (eps = 0 gives
+ *   NaN for a constant row, as the formula does).  Supported: d_model a
+ *   multiple of 4, at most 4096.  rows = 0 is a no-op.
+ */
+int mha_add_norm(const void* x, const void* sub, const void* gamma, const void* beta, float eps,
+                 void* out, int32_t dtype, int64_t rows, int64_t d_model, void* stream);
+
+/*
+ * The attention sub-layer with its Add & Norm:
+ *   out = LayerNorm(x_q + MultiHead(x_q, x_kv, x_kv))
+ * (the residual is the query-side input: for encoder-decoder attention the
+ * decoder stream).  Arguments as mha_forward, plus gamma and beta [d_model]
+ * (dtype) and eps as in mha_add_norm; d_model at most 4096.  The output
+ * projection adds the residual in its epilogue and keeps x_q + concat·Wo in
+ * fp32 (workspace) for the normalisation, so out is rounded once.
+ * workspace: at least mha_forward_add_norm_workspace_size() bytes (or NULL:
+ * allocated stream-ordered inside the call).
+ */
+int mha_forward_add_norm(const void* x_q, const void* x_kv, const void* Wq, const void* Wk,
+                         const void* Wv, const void* Wo, const void* gamma, const void* beta,
+                         float eps, void* out, int32_t dtype, int64_t B, int64_t n_q, int64_t n_k,
+                         int64_t d_model, int32_t h, int32_t mask_kind, const int32_t* kv_lens,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mha_forward_add_norm needs (0 for invalid sizes). */
+size_t mha_forward_add_norm_workspace_size(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model,
+                                           int32_t h, int32_t dtype);
+
 /* Static description of a status code (never NULL). */
 const char* mha_status_string(int status);
 

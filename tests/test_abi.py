@@ -41,7 +41,7 @@ def test_status_strings_and_version():
         s = M.status_string(code)
         assert s.startswith("MHA_ERR_"), s
     assert "unknown" in M.status_string(-99)
-    assert M.version() == 100
+    assert M.version() == 200
 
 
 def _sdpa(dtype=M.MHA_BF16, B=1, h=1, n_q=8, n_k=8, d_k=64, d_v=64, scale=0.125,
@@ -133,3 +133,70 @@ def test_workspace_size():
     assert need < 2 * (2 * B * n_q * dm + 2 * B * n_k * dm) + 4 * 256
     assert L.mha_forward_workspace_size(B, n_q, n_k, dm, 0, M.MHA_BF16) == 0
     assert L.mha_forward_workspace_size(B, n_q, n_k, 1000, 16, M.MHA_BF16) == 0
+
+
+def _an(dtype=M.MHA_BF16, rows=4, d=64, eps=1e-5, x=0x1000, sub=0x100000, g=0x200000,
+        b=0x300000, out=0x400000):
+    L = M.lib()
+    return L.mha_add_norm(x, sub, g, b, eps, out, dtype, rows, d, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=9), M.MHA_ERR_DTYPE),
+    (dict(rows=-1), M.MHA_ERR_SHAPE),
+    (dict(d=0), M.MHA_ERR_SHAPE),
+    (dict(d=66), M.MHA_ERR_UNSUPPORTED),          # not a multiple of 4
+    (dict(d=8192), M.MHA_ERR_UNSUPPORTED),        # above 4096
+    (dict(eps=-1.0), M.MHA_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), M.MHA_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), M.MHA_ERR_INVALID_ARG),
+    (dict(g=None), M.MHA_ERR_INVALID_ARG),
+    (dict(sub=None), M.MHA_ERR_INVALID_ARG),
+    (dict(x=0x1008), M.MHA_ERR_INVALID_ARG),      # not 16-byte aligned
+    (dict(out=0x1000 + 16), M.MHA_ERR_ALIAS),      # partial overlap with x
+    (dict(out=0x200000), M.MHA_ERR_ALIAS),         # overlaps gamma
+    (dict(out=0x300000 - 64), M.MHA_ERR_ALIAS),    # runs into beta
+])
+def test_add_norm_rejects(kw, code):
+    assert _an(**kw) == code
+    assert M.last_error() != ""
+
+
+def test_add_norm_zero_rows_is_noop():
+    assert _an(rows=0) == M.MHA_OK
+    assert _an(rows=0, x=None, out=None) == M.MHA_OK
+
+
+def _fan(dtype=M.MHA_BF16, B=2, n_q=8, n_k=8, d_model=128, h=2, eps=1e-5,
+         g=0x700000, b=0x710000, out=0x500000, ws=None, ws_bytes=0, x_kv=None):
+    L = M.lib()
+    return L.mha_forward_add_norm(0x1000, x_kv, 0x100000, 0x200000, 0x300000, 0x400000, g, b, eps,
+                                  out, dtype, B, n_q, n_k, d_model, h, 0, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(g=None), M.MHA_ERR_INVALID_ARG),
+    (dict(b=None), M.MHA_ERR_INVALID_ARG),
+    (dict(eps=-0.5), M.MHA_ERR_INVALID_ARG),
+    (dict(d_model=8192, h=128), M.MHA_ERR_UNSUPPORTED),   # above 4096
+    (dict(dtype=M.MHA_F32), M.MHA_ERR_UNSUPPORTED),
+    (dict(out=0x700000 - 16), M.MHA_ERR_ALIAS),          # out runs into gamma
+    (dict(g=0x700008), M.MHA_ERR_INVALID_ARG),            # misaligned gamma
+    (dict(ws=0x800000, ws_bytes=16), M.MHA_ERR_WORKSPACE),
+])
+def test_forward_add_norm_rejects(kw, code):
+    assert _fan(**kw) == code
+    assert M.last_error().startswith("mha_forward_add_norm")
+
+
+def test_forward_add_norm_workspace_size():
+    L = M.lib()
+    # z (fp32) fits below the concat: the same bytes as mha_forward
+    args = (8, 384, 512, 1024, 16, M.MHA_BF16)
+    assert L.mha_forward_add_norm_workspace_size(*args) == L.mha_forward_workspace_size(*args)
+    # few keys: Q/K/V are smaller than the fp32 rows, which go after the concat
+    B, n_q, n_k, dm = 2, 300, 20, 512
+    base = L.mha_forward_workspace_size(B, n_q, n_k, dm, 8, M.MHA_BF16)
+    need = L.mha_forward_add_norm_workspace_size(B, n_q, n_k, dm, 8, M.MHA_BF16)
+    assert need == base + B * n_q * dm * 4
+    assert L.mha_forward_add_norm_workspace_size(B, n_q, n_k, dm, 0, M.MHA_BF16) == 0

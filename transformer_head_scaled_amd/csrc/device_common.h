@@ -15,6 +15,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -47,6 +48,21 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   } else {
     f16x2 v = {(_Float16)a, (_Float16)b};
     return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// Four half-precision values (two dwords, element 0 in the low half of the
+// first) -> floats, exactly.  (fp16: one bit cast of the whole 8 bytes;
+// casting the two dwords to half pairs one by one was compiled as if both
+// held the first pair.)
+template <int DT>
+__device__ __forceinline__ f32x4 unpack4(u32x2 w) {
+  if constexpr (DT == DT_BF16) {
+    return f32x4{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xffff0000u),
+                 __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xffff0000u)};
+  } else {
+    const f16x4 h = __builtin_bit_cast(f16x4, w);
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
   }
 }
 

@@ -209,6 +209,27 @@ __global__ __launch_bounds__((TM / WTM) * (TN / WTN) * 64) void gemm_kernel(Gemm
     asm volatile("s_barrier" ::: "memory");
   }
 
+  if (P.R) {
+    // residual added, fp32 output in the plain [M, N] layout
+    const uint16_t* Rg = (const uint16_t*)P.R;
+    float* Cf = (float*)P.C;
+#pragma unroll
+    for (int j = 0; j < WM; ++j) {
+      const int m = m0 + wm * WTM + j * 32 + l32;
+      if (m >= P.M) continue;
+#pragma unroll
+      for (int i = 0; i < WN; ++i)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = n0 + wn * WTN + i * 32 + gq * 8 + hi * 4;
+          const f32x4 r = unpack4<DT>(*(const u32x2*)(Rg + (int64_t)m * P.ldr + n));
+          const f32x4 v = {acc[i][j][4 * gq] + r[0], acc[i][j][4 * gq + 1] + r[1],
+                           acc[i][j][4 * gq + 2] + r[2], acc[i][j][4 * gq + 3] + r[3]};
+          *(f32x4*)(Cf + (int64_t)m * P.c_st + n) = v;
+        }
+    }
+    return;
+  }
   // The head split is computed once per 32-column block.  A lane stores
   // columns 8·gq + 4·hi .. +3 of the block; with head_dim a multiple of 32
   // they all belong to the block's head, with head_dim 16 the block holds

@@ -32,11 +32,14 @@ int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t n_k, int
 //     + (n / head_dim) * c_sh + (n % head_dim)
 // which expresses both the head-split layout [B, h, n, d] and a plain
 // row-major [M, N] matrix.  head_dim is 16 or a multiple of 32.
+// With R set, the epilogue adds the residual R[m·ldr + n] (storage dtype)
+// and stores fp32 to C + m·c_st + n instead (the plain map only).
 struct GemmProblem {
   const void* A;
   const void* W;
   void* C;
-  int64_t lda, ldw;
+  const void* R;
+  int64_t lda, ldw, ldr;
   int64_t c_sb, c_st, c_sh;
   int32_t M, rows_per_b, head_dim, pad_;
 };
@@ -50,5 +53,22 @@ struct GemmArgs {
 
 // Chooses the tile shape from the problem sizes.
 hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t st);
+
+// out = LayerNorm(x + sub) per row of d features (contiguous rows):
+// z_f32 = false: x and sub in the storage dtype; true: z already holds
+// x + sub in fp32.  gamma, beta [d] and out in the storage dtype.
+constexpr int kAddNormMaxD = 4096;
+struct AddNormArgs {
+  const void* x;
+  const void* sub;
+  const void* z;
+  const void* gamma;
+  const void* beta;
+  void* out;
+  int64_t rows;
+  int32_t d;
+  float eps;
+};
+hipError_t launch_add_norm(const AddNormArgs& a, int dtype, bool z_f32, hipStream_t st);
 
 }  // namespace mha

@@ -65,6 +65,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
   size_t q, k, v, concat, total;
+  // mha_forward_add_norm: the fp32 x + concat·Wo rows, written after the
+  // attention has consumed Q/K/V, so at offset 0 when that region is large
+  // enough (it must not reach the concat, which the same GEMM reads)
+  size_t z, total_an;
 };
 
 WsLayout ws_layout(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model, int dtype) {
@@ -75,6 +79,9 @@ WsLayout ws_layout(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model, int dty
   w.v = align256(w.k + (size_t)(B * n_k * d_model) * es);
   w.concat = align256(w.v + (size_t)(B * n_k * d_model) * es);
   w.total = align256(w.concat + (size_t)(B * n_q * d_model) * es);
+  const size_t zbytes = align256((size_t)(B * n_q * d_model) * 4);
+  w.z = zbytes <= w.concat ? 0 : w.total;
+  w.total_an = w.z + zbytes > w.total ? w.z + zbytes : w.total;
   return w;
 }
 
@@ -104,7 +111,7 @@ const char* mha_status_string(int status) {
 
 const char* mha_last_error(void) { return g_err; }
 
-int mha_version(void) { return 100; }
+int mha_version(void) { return 200; }
 
 int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype, int64_t B,
              int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, float scale,
@@ -183,52 +190,68 @@ size_t mha_forward_workspace_size(int64_t B, int64_t n_q, int64_t n_k, int64_t d
   return ws_layout(B, n_q, n_k, d_model, dtype).total;
 }
 
-int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* Wk,
-                const void* Wv, const void* Wo, void* out, int32_t dtype, int64_t B,
-                int64_t n_q, int64_t n_k, int64_t d_model, int32_t h, int32_t mask_kind,
-                const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream) {
+// The sublayer; with an_gamma set (mha_forward_add_norm) also its Add &
+// Norm: the output projection's epilogue adds the residual x_q and writes
+// fp32 rows to the workspace, which the normalisation reads.
+static int forward_impl(const char* fn, const void* x_q, const void* x_kv, const void* Wq,
+                        const void* Wk, const void* Wv, const void* Wo, const void* an_gamma,
+                        const void* an_beta, float an_eps, void* out, int32_t dtype, int64_t B,
+                        int64_t n_q, int64_t n_k, int64_t d_model, int32_t h, int32_t mask_kind,
+                        const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const bool an = an_gamma != nullptr || an_beta != nullptr;
   if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16)
-    return fail(MHA_ERR_DTYPE, "mha_forward: dtype %d", (int)dtype);
+    return fail(MHA_ERR_DTYPE, "%s: dtype %d", fn, (int)dtype);
   if (mask_kind != MHA_MASK_NONE && mask_kind != MHA_MASK_CAUSAL)
-    return fail(MHA_ERR_INVALID_ARG, "mha_forward: mask_kind %d", (int)mask_kind);
+    return fail(MHA_ERR_INVALID_ARG, "%s: mask_kind %d", fn, (int)mask_kind);
   if (B < 0 || n_q < 0 || n_k < 0 || d_model <= 0 || h <= 0)
-    return fail(MHA_ERR_SHAPE, "mha_forward: negative or zero size");
+    return fail(MHA_ERR_SHAPE, "%s: negative or zero size", fn);
   if (d_model % h != 0)
-    return fail(MHA_ERR_SHAPE, "mha_forward: d_model %lld not divisible by h %d",
+    return fail(MHA_ERR_SHAPE, "%s: d_model %lld not divisible by h %d", fn,
                 (long long)d_model, (int)h);
   if (n_q > kMaxRows || n_k > kMaxRows || B > 65535 || d_model > 65536 ||
       B * n_q > ((int64_t)1 << 31) - 1 || B * n_k > ((int64_t)1 << 31) - 1)
-    return fail(MHA_ERR_SHAPE, "mha_forward: size beyond the supported range");
+    return fail(MHA_ERR_SHAPE, "%s: size beyond the supported range", fn);
   const bool self = (x_kv == nullptr || x_kv == x_q);
   if (self && n_k != n_q)
-    return fail(MHA_ERR_SHAPE, "mha_forward: self-attention needs n_k == n_q");
+    return fail(MHA_ERR_SHAPE, "%s: self-attention needs n_k == n_q", fn);
   if (mask_kind == MHA_MASK_CAUSAL && n_q != n_k)
-    return fail(MHA_ERR_SHAPE, "mha_forward: causal mask needs n_q == n_k");
-  if (dtype == MHA_F32) return fail(MHA_ERR_UNSUPPORTED, "mha_forward: f32 is not implemented");
+    return fail(MHA_ERR_SHAPE, "%s: causal mask needs n_q == n_k", fn);
+  if (dtype == MHA_F32) return fail(MHA_ERR_UNSUPPORTED, "%s: f32 is not implemented", fn);
   const int64_t d = d_model / h;
   if (d != 16 && d != 32 && d != 64 && d != 128)
-    return fail(MHA_ERR_UNSUPPORTED, "mha_forward: head dim %lld (needs 16, 32, 64 or 128)",
+    return fail(MHA_ERR_UNSUPPORTED, "%s: head dim %lld (needs 16, 32, 64 or 128)", fn,
                 (long long)d);
   if (d_model % 64 != 0)  // the projection GEMMs tile N and K by 64
-    return fail(MHA_ERR_UNSUPPORTED, "mha_forward: d_model %lld is not a multiple of 64",
+    return fail(MHA_ERR_UNSUPPORTED, "%s: d_model %lld is not a multiple of 64", fn,
                 (long long)d_model);
   if (n_k * d * 2 > kMaxBufferBytes)
-    return fail(MHA_ERR_UNSUPPORTED, "mha_forward: one head's K/V exceeds 2 GiB (n_k %lld)",
+    return fail(MHA_ERR_UNSUPPORTED, "%s: one head's K/V exceeds 2 GiB (n_k %lld)", fn,
                 (long long)n_k);
+  if (an) {
+    if (!std::isfinite(an_eps) || an_eps < 0.f)
+      return fail(MHA_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+    if (d_model > mha::kAddNormMaxD)
+      return fail(MHA_ERR_UNSUPPORTED, "%s: d_model %lld above %d", fn, (long long)d_model,
+                  mha::kAddNormMaxD);
+  }
   if (B == 0 || n_q == 0) return ok();
+  if (an && (!an_gamma || !an_beta || !aligned16(an_gamma) || !aligned16(an_beta)))
+    return fail(MHA_ERR_INVALID_ARG, "%s: gamma and beta must be 16-byte aligned device pointers", fn);
   if (!x_q || !Wq || !Wk || !Wv || !Wo || !out)
-    return fail(MHA_ERR_INVALID_ARG, "mha_forward: null tensor pointer");
+    return fail(MHA_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
   if (!aligned16(x_q) || !aligned16(x_kv) || !aligned16(Wq) || !aligned16(Wk) ||
       !aligned16(Wv) || !aligned16(Wo) || !aligned16(out) ||
       (reinterpret_cast<uintptr_t>(kv_lens) & 3) != 0)
-    return fail(MHA_ERR_INVALID_ARG, "mha_forward: tensors must be 16-byte aligned");
+    return fail(MHA_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
   const size_t es = elem_size(dtype);
   const WsLayout L = ws_layout(B, n_q, n_k, d_model, dtype);
-  if (workspace && workspace_bytes < L.total)
-    return fail(MHA_ERR_WORKSPACE, "mha_forward: workspace %zu bytes, needs %zu", workspace_bytes,
-                L.total);
+  const size_t ws_need = an ? L.total_an : L.total;
+  if (workspace && workspace_bytes < ws_need)
+    return fail(MHA_ERR_WORKSPACE, "%s: workspace %zu bytes, needs %zu", fn, workspace_bytes,
+                ws_need);
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
-    return fail(MHA_ERR_INVALID_ARG, "mha_forward: workspace not 256-byte aligned");
+    return fail(MHA_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
   const size_t wbytes = (size_t)(d_model * d_model) * es;
   const Range ro = range_of(out, (size_t)(B * n_q * d_model) * es);
   if (overlap(ro, range_of(x_q, (size_t)(B * n_q * d_model) * es)) ||
@@ -236,15 +259,17 @@ int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* W
       overlap(ro, range_of(Wq, wbytes)) || overlap(ro, range_of(Wk, wbytes)) ||
       overlap(ro, range_of(Wv, wbytes)) || overlap(ro, range_of(Wo, wbytes)) ||
       (kv_lens && overlap(ro, range_of(kv_lens, (size_t)B * 4))) ||
-      (workspace && overlap(ro, range_of(workspace, L.total))))
-    return fail(MHA_ERR_ALIAS, "mha_forward: out overlaps an input or the workspace");
+      (workspace && overlap(ro, range_of(workspace, ws_need))) ||
+      (an && (overlap(ro, range_of(an_gamma, (size_t)d_model * es)) ||
+              overlap(ro, range_of(an_beta, (size_t)d_model * es)))))
+    return fail(MHA_ERR_ALIAS, "%s: out overlaps an input or the workspace", fn);
 
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   bool owned = false;
   if (!ws) {
-    const hipError_t e = hipMallocAsync((void**)&ws, L.total, st);
-    if (e != hipSuccess) return hip_fail(e, "mha_forward workspace allocation");
+    const hipError_t e = hipMallocAsync((void**)&ws, ws_need, st);
+    if (e != hipSuccess) return hip_fail(e, "workspace allocation");
     owned = true;
   }
   const void* xkv = self ? x_q : x_kv;
@@ -303,17 +328,84 @@ int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* W
     o.K = (int32_t)d_model;
     o.nprob = 1;
     mha::GemmProblem& p = o.prob[0];
-    p.A = c_ws, p.W = Wo, p.C = out;
+    p.A = c_ws, p.W = Wo, p.C = an ? (void*)(ws + L.z) : out;
     p.lda = d_model, p.ldw = d_model;
     p.M = (int32_t)(B * n_q), p.rows_per_b = (int32_t)(B * n_q), p.head_dim = (int32_t)d_model;
     p.c_sb = 0, p.c_st = d_model, p.c_sh = 0;
+    if (an) p.R = x_q, p.ldr = d_model;  // z = x_q + concat·Wo, fp32
     e = mha::launch_gemm(o, dtype, st);
+  }
+  // (4) Add & Norm: out = LayerNorm(z)
+  if (an && e == hipSuccess) {
+    mha::AddNormArgs a{};
+    a.z = ws + L.z, a.gamma = an_gamma, a.beta = an_beta, a.out = out;
+    a.rows = B * n_q, a.d = (int32_t)d_model, a.eps = an_eps;
+    e = mha::launch_add_norm(a, dtype, true, st);
   }
   if (owned) {
     const hipError_t e2 = hipFreeAsync(ws, st);
     if (e == hipSuccess) e = e2;
   }
-  if (e != hipSuccess) return hip_fail(e, "mha_forward launch");
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* Wk,
+                const void* Wv, const void* Wo, void* out, int32_t dtype, int64_t B,
+                int64_t n_q, int64_t n_k, int64_t d_model, int32_t h, int32_t mask_kind,
+                const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl("mha_forward", x_q, x_kv, Wq, Wk, Wv, Wo, nullptr, nullptr, 0.f, out, dtype,
+                      B, n_q, n_k, d_model, h, mask_kind, kv_lens, workspace, workspace_bytes,
+                      stream);
+}
+
+int mha_forward_add_norm(const void* x_q, const void* x_kv, const void* Wq, const void* Wk,
+                         const void* Wv, const void* Wo, const void* gamma, const void* beta,
+                         float eps, void* out, int32_t dtype, int64_t B, int64_t n_q, int64_t n_k,
+                         int64_t d_model, int32_t h, int32_t mask_kind, const int32_t* kv_lens,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!gamma || !beta) return fail(MHA_ERR_INVALID_ARG, "mha_forward_add_norm: null gamma or beta");
+  return forward_impl("mha_forward_add_norm", x_q, x_kv, Wq, Wk, Wv, Wo, gamma, beta, eps, out,
+                      dtype, B, n_q, n_k, d_model, h, mask_kind, kv_lens, workspace,
+                      workspace_bytes, stream);
+}
+
+size_t mha_forward_add_norm_workspace_size(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model,
+                                           int32_t h, int32_t dtype) {
+  if (mha_forward_workspace_size(B, n_q, n_k, d_model, h, dtype) == 0) return 0;
+  return ws_layout(B, n_q, n_k, d_model, dtype).total_an;
+}
+
+int mha_add_norm(const void* x, const void* sub, const void* gamma, const void* beta, float eps,
+                 void* out, int32_t dtype, int64_t rows, int64_t d_model, void* stream) {
+  if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16)
+    return fail(MHA_ERR_DTYPE, "mha_add_norm: dtype %d", (int)dtype);
+  if (rows < 0 || d_model <= 0) return fail(MHA_ERR_SHAPE, "mha_add_norm: negative or zero size");
+  if (rows > ((int64_t)1 << 33)) return fail(MHA_ERR_SHAPE, "mha_add_norm: rows beyond the supported range");
+  if (d_model % 4 != 0 || d_model > mha::kAddNormMaxD)
+    return fail(MHA_ERR_UNSUPPORTED, "mha_add_norm: d_model %lld (needs a multiple of 4, at most %d)",
+                (long long)d_model, mha::kAddNormMaxD);
+  if (!std::isfinite(eps) || eps < 0.f)
+    return fail(MHA_ERR_INVALID_ARG, "mha_add_norm: eps must be finite and >= 0");
+  if (rows == 0) return ok();
+  if (!x || !sub || !gamma || !beta || !out)
+    return fail(MHA_ERR_INVALID_ARG, "mha_add_norm: null pointer");
+  if (!aligned16(x) || !aligned16(sub) || !aligned16(gamma) || !aligned16(beta) || !aligned16(out))
+    return fail(MHA_ERR_INVALID_ARG, "mha_add_norm: tensors must be 16-byte aligned");
+  const size_t es = elem_size(dtype);
+  const size_t rb = (size_t)(rows * d_model) * es;
+  const Range ro = range_of(out, rb);
+  // in place (out == x or out == sub) is allowed: a row is read whole
+  // before it is written; any other overlap is not
+  if ((out != x && overlap(ro, range_of(x, rb))) || (out != sub && overlap(ro, range_of(sub, rb))) ||
+      overlap(ro, range_of(gamma, (size_t)d_model * es)) ||
+      overlap(ro, range_of(beta, (size_t)d_model * es)))
+    return fail(MHA_ERR_ALIAS, "mha_add_norm: out partially overlaps x or sub, or overlaps gamma/beta");
+  mha::AddNormArgs a{};
+  a.x = x, a.sub = sub, a.gamma = gamma, a.beta = beta, a.out = out;
+  a.rows = rows, a.d = (int32_t)d_model, a.eps = eps;
+  const hipError_t e = mha::launch_add_norm(a, dtype, false, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mha_add_norm launch");
   return ok();
 }
 

@@ -25,7 +25,8 @@ MHA_ERR_ALIAS = -6
 MHA_ERR_HIP = -7
 
 # every symbol include/mha.h declares
-EXPORTS = ("mha_sdpa", "mha_forward", "mha_forward_workspace_size", "mha_status_string",
+EXPORTS = ("mha_sdpa", "mha_forward", "mha_forward_workspace_size", "mha_add_norm",
+           "mha_forward_add_norm", "mha_forward_add_norm_workspace_size", "mha_status_string",
            "mha_last_error", "mha_version")
 
 _lib = None
@@ -54,6 +55,13 @@ def lib():
     L.mha_forward.restype = ctypes.c_int
     L.mha_forward_workspace_size.argtypes = [i64, i64, i64, i64, i32, i32]
     L.mha_forward_workspace_size.restype = ctypes.c_size_t
+    L.mha_add_norm.argtypes = [vp, vp, vp, vp, f32, vp, i32, i64, i64, vp]
+    L.mha_add_norm.restype = ctypes.c_int
+    L.mha_forward_add_norm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, i64, i64,
+                                       i64, i64, i32, i32, vp, vp, ctypes.c_size_t, vp]
+    L.mha_forward_add_norm.restype = ctypes.c_int
+    L.mha_forward_add_norm_workspace_size.argtypes = [i64, i64, i64, i64, i32, i32]
+    L.mha_forward_add_norm_workspace_size.restype = ctypes.c_size_t
     L.mha_status_string.argtypes = [ctypes.c_int]
     L.mha_status_string.restype = ctypes.c_char_p
     L.mha_last_error.argtypes = []
@@ -171,4 +179,59 @@ def forward(x_q, Wq, Wk, Wv, Wo, h, x_kv=None, mask="none", kv_lens=None, out=No
                              _ptr(out), dtype_code(x_q), B, n_q, n_k, d_model, int(h),
                              _mask_code(mask), _ptr(lens), _ptr(workspace), ws_bytes,
                              _stream(stream)))
+    return out
+
+
+def add_norm_workspace_size(B, n_q, n_k, d_model, h, dtype):
+    return int(lib().mha_forward_add_norm_workspace_size(B, n_q, n_k, d_model, h, dtype))
+
+
+def add_norm(x, sub, gamma, beta, eps=1e-5, out=None, stream=None):
+    """mha_add_norm: out = LayerNorm(x + sub) over the last axis.  x, sub
+    [..., d_model]; gamma, beta [d_model]; all one dtype.  ``out`` may be x
+    or sub (in place)."""
+    import torch
+    for n, t in (("x", x), ("sub", sub), ("gamma", gamma), ("beta", beta)):
+        _contig(t, n)
+    d_model = x.shape[-1]
+    if tuple(sub.shape) != tuple(x.shape):
+        raise ValueError("x and sub must have the same shape")
+    for n, t in (("gamma", gamma), ("beta", beta)):
+        if tuple(t.shape) != (d_model,):
+            raise ValueError(f"{n} must be [{d_model}]")
+    if out is None:
+        out = torch.empty_like(x)
+    _contig(out, "out")
+    rows = x.numel() // d_model if d_model else 0
+    _check(lib().mha_add_norm(_ptr(x), _ptr(sub), _ptr(gamma), _ptr(beta), float(eps), _ptr(out),
+                              dtype_code(x), rows, d_model, _stream(stream)))
+    return out
+
+
+def forward_add_norm(x_q, Wq, Wk, Wv, Wo, gamma, beta, h, eps=1e-5, x_kv=None, mask="none",
+                     kv_lens=None, out=None, workspace=None, stream=None):
+    """mha_forward_add_norm: LayerNorm(x_q + MultiHead(x_q, x_kv, x_kv)).
+    Arguments as forward(), plus gamma, beta [d_model] and eps."""
+    import torch
+    for n, t in (("x_q", x_q), ("x_kv", x_kv), ("Wq", Wq), ("Wk", Wk), ("Wv", Wv), ("Wo", Wo),
+                 ("gamma", gamma), ("beta", beta)):
+        _contig(t, n)
+    B, n_q, d_model = x_q.shape
+    n_k = n_q if x_kv is None else x_kv.shape[1]
+    for n, t in (("Wq", Wq), ("Wk", Wk), ("Wv", Wv), ("Wo", Wo)):
+        if tuple(t.shape) != (d_model, d_model):
+            raise ValueError(f"{n} must be [{d_model}, {d_model}]")
+    for n, t in (("gamma", gamma), ("beta", beta)):
+        if tuple(t.shape) != (d_model,):
+            raise ValueError(f"{n} must be [{d_model}]")
+    if out is None:
+        out = torch.empty((B, n_q, d_model), dtype=x_q.dtype, device=x_q.device)
+    _contig(out, "out")
+    lens = _lens(kv_lens, B, "kv_lens")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mha_forward_add_norm(_ptr(x_q), _ptr(x_kv), _ptr(Wq), _ptr(Wk), _ptr(Wv),
+                                      _ptr(Wo), _ptr(gamma), _ptr(beta), float(eps), _ptr(out),
+                                      dtype_code(x_q), B, n_q, n_k, d_model, int(h),
+                                      _mask_code(mask), _ptr(lens), _ptr(workspace), ws_bytes,
+                                      _stream(stream)))
     return out
