@@ -95,8 +95,9 @@ def other_configs(dev, stream, iters=100):
     working set fits the 256 MB last-level cache): mha_forward self
     attention with key padding (B 32, n 64, d_model 512, h 8), causal SDPA
     (B 16, h 8, n 512), mha_forward cross attention (B 8, n_q 384, n_k 512,
-    d_model 1024, h 16), and one decoding step (B 64, h 8, one query row
-    against a 2048-entry key/value cache, HBM-bound).  Rates use algorithmic
+    d_model 1024, h 16) also with its Add & Norm, the Add & Norm alone on
+    those rows, and one decoding step (B 64, h 8, one query row against a
+    2048-entry key/value cache, HBM-bound).  Rates use algorithmic
     flops and bytes.  Cold calls follow a read of a 512 MB buffer (a read
     leaves clean lines; an overwrite would leave dirty ones that the timed
     call then writes back)."""
@@ -136,6 +137,43 @@ def other_configs(dev, stream, iters=100):
             cmed, cmn = time_calls(call, stream, max(iters // 4, 10), flush)
             entry["us_median_cold"] = round(cmed, 2)
         res[w["name"]] = entry
+    # Add & Norm on the big cross-attention workload: the sub-layer with its
+    # residual and layer normalisation in one call, and the normalisation
+    # alone (HBM-bound: x and sub read, out written once)
+    w = synth.WORKLOADS[4]
+    ins, _ = synth.workload_inputs(4)
+    t = {k: dev_t(v[0]) for k, v in ins.items()}
+    B, n_q, n_k, dm, h = w["B"], w["n_q"], w["n_k"], w["d_model"], w["h"]
+    gamma = torch.ones(dm, dtype=torch.bfloat16, device=dev)
+    beta = torch.zeros(dm, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(libmha.add_norm_workspace_size(B, n_q, n_k, dm, h, 1), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, n_q, dm), dtype=torch.bfloat16, device=dev)
+
+    def call_fan():
+        libmha.forward_add_norm(t["x_q"], t["Wq"], t["Wk"], t["Wv"], t["Wo"], gamma, beta, h,
+                                x_kv=t["x_kv"], out=out, workspace=ws, stream=stream)
+    for _ in range(20):
+        call_fan()
+    med, mn = time_calls(call_fan, stream, iters)
+    res[w["name"] + "_add_norm"] = {"call": "mha_forward_add_norm", "us_median": round(med, 2),
+                                    "us_min": round(mn, 2)}
+    sub = torch.empty_like(out).normal_()
+
+    def call_an():
+        libmha.add_norm(t["x_q"], sub, gamma, beta, out=out, stream=stream)
+    for _ in range(20):
+        call_an()
+    med, mn = time_calls(call_an, stream, iters)
+    cmed, _ = time_calls(call_an, stream, max(iters // 4, 10), flush)
+    nbytes = 3 * B * n_q * dm * 2 + 2 * dm * 2
+    res["add_norm_bf16_rows3072_d1024"] = {
+        "call": "mha_add_norm", "us_median": round(med, 2), "us_min": round(mn, 2),
+        "us_median_cold": round(cmed, 2), "gbs": round(nbytes / (med * 1e-6) / 1e9, 1),
+        "gbs_cold": round(nbytes / (cmed * 1e-6) / 1e9, 1),
+        "hbm_frac_cold": round(nbytes / (cmed * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "bytes": nbytes}
+    del t, ws, out, sub
+
     w = synth.WORKLOADS[3]
     ins, _ = synth.workload_inputs(3)
     Q, K, V = (dev_t(ins[k][0]) for k in "QKV")

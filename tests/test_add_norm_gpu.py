@@ -2,9 +2,15 @@
 x + sub) and mha_forward_add_norm (the attention sub-layer with its residual
 connection and layer normalisation).
 
-Tolerance (max-abs): 2e-2 for bf16/fp16 storage, 1e-5 for fp32 (mha_add_norm
-only).  The pins of ``tests/pins.py`` re-run through the API; their inputs
-are exact in every storage dtype.
+Tolerance: max-abs 2e-2 for bf16/fp16 storage (1e-5 for fp32, mha_add_norm
+only) on top of the output's own final rounding, REL·|expected| with REL =
+2^-8 for bf16 and 2^-11 for fp16 (twice the unit roundoff).  Layer
+normalisation outputs reach |y| ~ 5-8 (unit variance times the gain), where
+one bf16 rounding alone is up to 0.016-0.03, more than the attention
+outputs' 2e-2 was set for (|O| <= ~2); the absolute part still bounds what
+the path computes before that rounding.  The pins of ``tests/pins.py``
+re-run through the API with the plain max-abs bound; their inputs and most
+of their outputs are exact or small in every storage dtype.
 """
 
 import numpy as np
@@ -23,11 +29,17 @@ def _gpu():
     require_gpu()
 
 
+REL = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 0.0}
+
+
 def _check(got, exp, dtype, what):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
-    err = float(np.max(np.abs(got - exp))) if got.size else 0.0
-    print(f"[parity] {what}: max-abs {err:.3e} (tol {TOL[dtype]:.0e})", flush=True)
-    assert err <= TOL[dtype], f"{what}: max-abs {err:.3e} > {TOL[dtype]}"
+    excess = np.abs(got - exp) - REL[dtype] * np.abs(exp)
+    err = float(np.max(excess)) if got.size else 0.0
+    raw = float(np.max(np.abs(got - exp))) if got.size else 0.0
+    print(f"[parity] {what}: max-abs {raw:.3e}, beyond the output rounding {err:.3e} "
+          f"(tol {TOL[dtype]:.0e})", flush=True)
+    assert err <= TOL[dtype], f"{what}: error beyond output rounding {err:.3e} > {TOL[dtype]}"
 
 
 def _dev(a, dtype):
