@@ -38,6 +38,7 @@ from .attention import (  # noqa: F401
     MASK_CAUSAL,
     MASK_NONE,
     attention_head,
+    band,
     mha,
     scores,
     sdpa,

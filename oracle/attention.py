@@ -44,6 +44,26 @@ def visible(n_q, n_k, mask_kind=MASK_NONE, kv_len=None):
     return vis
 
 
+def band(n_q, n_k, left, right):
+    """Boolean [n_q, n_k]: does key c lie in the neighbourhood of query r,
+    r - left <= c <= r + right?
+
+    nickwang.xyz §4 (Table 1, the "Auto-attention restreinte" row, and the
+    text after it): for very long sequences, self-attention may be
+    restricted to a neighbourhood of size r centred on the output position,
+    at O(r·n·d) per layer.  The window is given here by its two reaches from
+    the query position: the centred neighbourhood of size 2w + 1 is
+    left = right = w; left >= n_k with right = 0 sees exactly what the causal
+    mask lets through.  Positions are absolute indices of the query and key
+    sequences.
+    """
+    if left < 0 or right < 0:
+        raise ValueError("window reaches must be >= 0")
+    r = np.arange(n_q)[:, None]
+    c = np.arange(n_k)[None, :]
+    return (c >= r - int(left)) & (c <= r + int(right))
+
+
 def scores(q, k, scale):
     """S = scale · Q·Kᵀ for one head (nickwang.xyz, §3.2.1 eq. (1): the
     compatibility of each query with each key is their dot product, divided
@@ -96,22 +116,26 @@ def weighted_sum(p, vis, v):
     return out
 
 
-def attention_head(q, k, v, scale, mask_kind=MASK_NONE, kv_len=None):
-    """One head of eq. (1): returns (O [n_q, d_v], P [n_q, n_k])."""
+def attention_head(q, k, v, scale, mask_kind=MASK_NONE, kv_len=None, window=None):
+    """One head of eq. (1): returns (O [n_q, d_v], P [n_q, n_k]).  ``window``
+    is None or (left, right): restricted attention, see ``band``."""
     n_q, n_k = q.shape[0], k.shape[0]
     vis = visible(n_q, n_k, mask_kind, kv_len)
+    if window is not None:
+        vis = vis & band(n_q, n_k, window[0], window[1])
     s = scores(q, k, scale)
     p = softmax_rows(s, vis)
     return weighted_sum(p, vis, v), p
 
 
-def sdpa(Q, K, V, scale, mask_kind=MASK_NONE, seq_lens=None):
+def sdpa(Q, K, V, scale, mask_kind=MASK_NONE, seq_lens=None, window=None):
     """Batched scaled dot-product attention, float64.
 
     Q [B, h, n_q, d_k], K [B, h, n_k, d_k], V [B, h, n_k, d_v] (any real
     dtype, upcast exactly).  ``seq_lens`` is None or B integers: the valid key
-    count of each batch entry.  Returns O [B, h, n_q, d_v] float64.  Every
-    (batch, head) pair is an independent eq. (1).
+    count of each batch entry.  ``window`` is None or (left, right), the
+    restricted attention of ``band``.  Returns O [B, h, n_q, d_v] float64.
+    Every (batch, head) pair is an independent eq. (1).
     """
     Q = np.asarray(Q)
     K = np.asarray(K)
@@ -123,7 +147,7 @@ def sdpa(Q, K, V, scale, mask_kind=MASK_NONE, seq_lens=None):
         kv_len = None if seq_lens is None else int(seq_lens[b])
         for i in range(h):
             out[b, i], _ = attention_head(Q[b, i], K[b, i], V[b, i], scale,
-                                          mask_kind, kv_len)
+                                          mask_kind, kv_len, window)
     return out
 
 

@@ -21,12 +21,13 @@ def _dot(a, b):
     return t
 
 
-def head(q, k, v, scale, causal, kv_len):
+def head(q, k, v, scale, causal, kv_len, window=None):
     n_q, n_k, d_v = len(q), len(k), len(v[0]) if len(v) else 0
     lim = n_k if kv_len is None else min(max(int(kv_len), 0), n_k)
     out = [[0.0] * d_v for _ in range(n_q)]
     for r in range(n_q):
-        cols = [c for c in range(n_k) if c < lim and (not causal or c <= r)]
+        cols = [c for c in range(n_k) if c < lim and (not causal or c <= r)
+                and (window is None or (abs(c - r) <= window[0] if c < r else c - r <= window[1]))]
         s = {c: scale * _dot(q[r], k[c]) for c in cols}
         for c in cols:
             w = 1.0 / sum(math.exp(s[c2] - s[c]) for c2 in cols)
@@ -35,12 +36,14 @@ def head(q, k, v, scale, causal, kv_len):
     return out
 
 
-def sdpa(Q, K, V, scale, causal=False, seq_lens=None):
-    """Q, K, V nested lists or arrays [B][h][n][d]; returns nested lists."""
+def sdpa(Q, K, V, scale, causal=False, seq_lens=None, window=None):
+    """Q, K, V nested lists or arrays [B][h][n][d]; returns nested lists.
+    ``window`` (left, right): key c within left positions before or right
+    positions after the query (restricted attention)."""
     out = []
     for b in range(len(Q)):
         kv_len = None if seq_lens is None else seq_lens[b]
-        out.append([head(Q[b][i], K[b][i], V[b][i], scale, causal, kv_len)
+        out.append([head(Q[b][i], K[b][i], V[b][i], scale, causal, kv_len, window)
                     for i in range(len(Q[b]))])
     return out
 

@@ -12,6 +12,8 @@ Implementation signatures:
   sdpa_fn(Q, K, V, scale, mask_kind, seq_lens) -> ndarray [B, h, n_q, d_v]
   mha_fn(x_q, x_kv, Wq, Wk, Wv, Wo, h, mask_kind, kv_lens) -> [B, n_q, d_model]
   add_norm_fn(x, sub, gamma, beta, eps) -> [rows, d]   (LayerNorm(x + sub))
+  window_fn(Q, K, V, scale, left, right, seq_lens) -> [B, h, n_q, d_v]
+      (restricted attention: key c visible to query r iff r-left <= c <= r+right)
 Inputs are float64 numpy arrays; an implementation that stores lower
 precision rounds them itself, and ``rnd`` (a function array -> array) lets a
 pin build its expected value from the rounded inputs.
@@ -400,6 +402,71 @@ def pin_mha_single_head(mha_fn, sdpa_fn, atol=1e-10):
 
 MHA_PINS = [pin_mha_shapes, pin_mha_head_blocks, pin_mha_head_permutation,
             pin_mha_single_head]
+
+
+# ---- restricted attention ([N] §4: Table 1's "Auto-attention restreinte"
+# row and the text after it -- a neighbourhood of the output position)
+
+def _qkv(rs, B, h, n_q, n_k, d, rnd):
+    return (rnd(rs.standard_normal((B, h, n_q, d))), rnd(rs.standard_normal((B, h, n_k, d))),
+            rnd(rs.standard_normal((B, h, n_k, d))))
+
+
+def pin_window_covering_is_unmasked(window_fn, sdpa_fn, atol=1e-12, rnd=_ident):
+    """A window that reaches every key is plain attention (with and without
+    key padding)."""
+    rs = np.random.RandomState(21)
+    Q, K, V = _qkv(rs, 2, 2, 9, 13, 8, rnd)
+    for lens in (None, [5, 13]):
+        _close(window_fn(Q, K, V, 0.3, 13, 13, lens), sdpa_fn(Q, K, V, 0.3, NONE, lens), atol,
+               f"covering window, lens {lens}")
+
+
+def pin_window_left_unbounded_is_causal(window_fn, sdpa_fn, atol=1e-12, rnd=_ident):
+    """Reaching back to the first key and not forward at all is the causal
+    mask."""
+    rs = np.random.RandomState(22)
+    Q, K, V = _qkv(rs, 1, 3, 11, 11, 8, rnd)
+    _close(window_fn(Q, K, V, 0.5, 11, 0, None), sdpa_fn(Q, K, V, 0.5, CAUSAL, None), atol,
+           "window (n, 0)")
+
+
+def pin_window_zero_width(window_fn, atol=1e-12, rnd=_ident):
+    """Window (0, 0): query r sees key r alone, weight 1, so O[r] = V[r];
+    query rows past the last key see nothing and give 0."""
+    rs = np.random.RandomState(23)
+    Q, K, V = _qkv(rs, 2, 1, 7, 5, 8, rnd)
+    O = np.asarray(window_fn(Q, K, V, 0.7, 0, 0, None), dtype=np.float64)
+    _close(O[:, :, :5], V, atol, "O[r] = V[r]")
+    _close(O[:, :, 5:], np.zeros_like(O[:, :, 5:]), atol, "rows with no key")
+
+
+def pin_window_rows_are_slices(window_fn, sdpa_fn, atol=1e-12, rnd=_ident):
+    """Row r of the windowed attention is plain attention of q_r over the
+    keys r - left .. r + right (clipped to the sequence)."""
+    rs = np.random.RandomState(24)
+    n, left, right = 12, 2, 3
+    Q, K, V = _qkv(rs, 1, 1, n, n, 8, rnd)
+    O = np.asarray(window_fn(Q, K, V, 0.4, left, right, None), dtype=np.float64)
+    for r in (0, 1, 5, 9, 11):
+        lo, hi = max(0, r - left), min(n, r + right + 1)
+        o = sdpa_fn(Q[:, :, r:r + 1], K[:, :, lo:hi], V[:, :, lo:hi], 0.4, NONE, None)
+        _close(O[:, :, r:r + 1], o, atol, f"row {r}")
+
+
+def pin_window_outside_ignored(window_fn, atol=0.0, rnd=_ident):
+    """Keys outside every query's window have no effect, NaN included."""
+    rs = np.random.RandomState(25)
+    Q, K, V = _qkv(rs, 1, 2, 5, 12, 8, rnd)
+    clean = np.asarray(window_fn(Q, K, V, 0.6, 1, 1, None), dtype=np.float64)
+    K2, V2 = K.copy(), V.copy()
+    K2[:, :, 6:] = np.nan
+    V2[:, :, 6:] = np.nan
+    _close(window_fn(Q, K2, V2, 0.6, 1, 1, None), clean, atol, "NaN beyond every window")
+
+
+WINDOW_PINS = [pin_window_covering_is_unmasked, pin_window_left_unbounded_is_causal,
+               pin_window_zero_width, pin_window_rows_are_slices, pin_window_outside_ignored]
 
 
 # ---- Add & Norm ([N], the section on the encoder and decoder stacks, paper

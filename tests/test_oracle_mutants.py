@@ -275,3 +275,50 @@ def test_add_norm_unmutated_copy_passes():
     good = _add_norm_variant(None)
     for pin in pins.LN_PINS:
         pin(good)
+
+
+# ---- band mutants: the window step with one planted mistake each
+
+_real_band = A.band
+
+
+def _band_right_exclusive(n_q, n_k, left, right):
+    r = np.arange(n_q)[:, None]
+    c = np.arange(n_k)[None, :]
+    return (c >= r - left) & (c < r + right)
+
+
+def _band_swapped(n_q, n_k, left, right):
+    return _real_band(n_q, n_k, right, left)
+
+
+def _band_ignored(n_q, n_k, left, right):
+    return np.ones((n_q, n_k), dtype=bool)
+
+
+def _band_left_short(n_q, n_k, left, right):
+    return _real_band(n_q, n_k, max(left - 1, 0), right)
+
+
+BAND_MUTANTS = {"right_exclusive": _band_right_exclusive, "swapped": _band_swapped,
+                "ignored": _band_ignored, "left_short": _band_left_short}
+
+
+@pytest.mark.parametrize("name", sorted(BAND_MUTANTS))
+def test_band_mutant_is_caught(name, monkeypatch):
+    import inspect
+    monkeypatch.setattr(A, "band", BAND_MUTANTS[name])
+
+    def window(Q, K, V, scale, left, right, lens):
+        return oracle.sdpa(Q, K, V, scale, 0, lens, window=(left, right))
+    failed = []
+    for pin in pins.WINDOW_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                if "sdpa_fn" in inspect.signature(pin).parameters:
+                    pin(window, _sdpa)
+                else:
+                    pin(window)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"

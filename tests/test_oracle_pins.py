@@ -227,3 +227,49 @@ def test_mha_add_norm_torch_fp64():
     ref = F.layer_norm(xt + attn, (d_model,), t(g), t(b), 1e-5).numpy().transpose(1, 0, 2)
     got = oracle.mha_add_norm(x, None, Wq, Wk, Wv, Wo, g, b, 1e-5, h)
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+
+
+# ---- restricted attention (oracle.band)
+
+def _window(Q, K, V, scale, left, right, lens):
+    return oracle.sdpa(Q, K, V, scale, oracle.MASK_NONE, lens, window=(left, right))
+
+
+@pytest.mark.parametrize("pin", pins.WINDOW_PINS, ids=lambda p: p.__name__)
+def test_window_pin(pin):
+    import inspect
+    if "sdpa_fn" in inspect.signature(pin).parameters:
+        pin(_window, _sdpa)
+    else:
+        pin(_window)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_brute_force_window(seed):
+    rs = np.random.default_rng(700 + seed)
+    B, h = int(rs.integers(1, 3)), int(rs.integers(1, 3))
+    n_q, n_k = int(rs.integers(1, 10)), int(rs.integers(1, 10))
+    d = int(rs.integers(1, 5))
+    Q, K, V = (rs.standard_normal((B, h, n, d)) for n in (n_q, n_k, n_k))
+    left, right = int(rs.integers(0, 5)), int(rs.integers(0, 5))
+    lens = rs.integers(0, n_k + 1, size=B) if seed % 2 else None
+    got = oracle.sdpa(Q, K, V, 0.5, oracle.MASK_NONE, lens, window=(left, right))
+    exp = np.asarray(brute.sdpa(Q, K, V, 0.5, False, lens, window=(left, right)))
+    np.testing.assert_allclose(got, exp, rtol=0, atol=ATOL)
+
+
+def test_window_torch_fp64():
+    """torch's CPU float64 scaled_dot_product_attention with the band as a
+    boolean mask (rows with at least one visible key)."""
+    import torch.nn.functional as F
+    rs = np.random.default_rng(701)
+    B, h, n, d, left, right = 2, 3, 40, 16, 5, 2
+    Q, K, V = (rs.standard_normal((B, h, n, d)) for _ in range(3))
+    r = np.arange(n)[:, None]
+    c = np.arange(n)[None, :]
+    allow = (c >= r - left) & (c <= r + right)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(Q), torch.from_numpy(K),
+                                         torch.from_numpy(V), attn_mask=torch.from_numpy(allow),
+                                         scale=0.25).numpy()
+    got = oracle.sdpa(Q, K, V, 0.25, oracle.MASK_NONE, None, window=(left, right))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
