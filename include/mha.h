@@ -90,6 +90,22 @@ int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype
              int32_t mask_kind, const int32_t* seq_lens, void* stream);
 
 /*
+ * Restricted attention, [N] §4 (Table 1, "Auto-attention restreinte", and
+ * the text after it): attention limited to a neighbourhood of the output
+ * position.  As mha_sdpa without a mask kind, plus the window: key c is
+ * visible to query r iff r - left <= c <= r + right (positions are absolute
+ * indices; left, right >= 0, else MHA_ERR_INVALID_ARG).  The centred
+ * neighbourhood of size 2w + 1 is left = right = w; left >= n_q - 1 with
+ * right = 0 is the causal mask; seq_lens masks keys as in mha_sdpa.  A row
+ * whose window holds no valid key gives 0.  Only the key tiles inside some
+ * row's window are read.  Supported: as mha_sdpa.
+ */
+int mha_sdpa_window(const void* Q, const void* K, const void* V, void* O, int32_t dtype,
+                    int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v,
+                    float scale, int64_t left, int64_t right, const int32_t* seq_lens,
+                    void* stream);
+
+/*
  * Multi-head attention sublayer, [N] §3.2.2 ("Attention multi-têtes"):
  *   out = Concat(head_1, ..., head_h) · Wo,
  *   head_i = Attention(x_q·Wq_i, x_kv·Wk_i, x_kv·Wv_i) with scale 1/sqrt(d_k).

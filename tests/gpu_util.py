@@ -73,3 +73,21 @@ def gpu_sdpa(dtype):
         torch.cuda.synchronize()
         return from_dev(out)[..., :d_v]
     return fn, rnd
+
+
+def gpu_sdpa_window(dtype):
+    """window_fn for the pins: rounds inputs to ``dtype`` (zero-padding the
+    head dim as gpu_sdpa does) and runs mha_sdpa_window."""
+    def fn(Q, K, V, scale, left, right, lens):
+        Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
+        B, h, n_q, d = Q.shape
+        n_k, d_v = K.shape[2], V.shape[3]
+        dpad = 64 if dtype != "f32" else max(16, 1 << max(0, (max(d, d_v) - 1)).bit_length())
+        Qp = np.zeros((B, h, n_q, dpad)); Qp[..., :d] = Q
+        Kp = np.zeros((B, h, n_k, dpad)); Kp[..., :d] = K
+        Vp = np.zeros((B, h, n_k, dpad)); Vp[..., :d_v] = V
+        tq, tk, tv = (to_dev(rounded(a, dtype)[0], dtype) for a in (Qp, Kp, Vp))
+        out = libmha.sdpa_window(tq, tk, tv, left, right, scale=scale, seq_lens=lens_dev(lens))
+        torch.cuda.synchronize()
+        return from_dev(out)[..., :d_v]
+    return fn

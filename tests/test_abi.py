@@ -200,3 +200,24 @@ def test_forward_add_norm_workspace_size():
     need = L.mha_forward_add_norm_workspace_size(B, n_q, n_k, dm, 8, M.MHA_BF16)
     assert need == base + B * n_q * dm * 4
     assert L.mha_forward_add_norm_workspace_size(B, n_q, n_k, dm, 0, M.MHA_BF16) == 0
+
+
+def _win(left=1, right=1, dtype=M.MHA_BF16, n_q=8, n_k=8, O=0x300000):
+    L = M.lib()
+    return L.mha_sdpa_window(0x1000, 0x100000, 0x200000, O, dtype, 1, 1, n_q, n_k, 64, 64, 0.125,
+                             left, right, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(left=-1), M.MHA_ERR_INVALID_ARG),
+    (dict(right=-5), M.MHA_ERR_INVALID_ARG),
+    (dict(O=0x1000), M.MHA_ERR_ALIAS),
+    (dict(dtype=4), M.MHA_ERR_DTYPE),
+])
+def test_window_rejects(kw, code):
+    assert _win(**kw) == code
+    assert M.last_error().startswith("mha_sdpa_window")
+
+
+def test_window_zero_rows_is_noop():
+    assert _win(n_q=0) == M.MHA_OK

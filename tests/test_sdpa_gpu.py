@@ -201,6 +201,25 @@ DECODE_CASES = [
 ]
 
 
+def test_causal_nan_values_past_a_waves_rows():
+    """Causal [1,2,200,200] (two-wave workgroups, each wave a pair of 32-row
+    blocks) with the value rows 160.. set to NaN: rows below 160 never see
+    them, and the wave whose highest block ends at row 159 loads keys
+    160..191 with its diagonal tile -- their weights are 0 and their values
+    are cleared before P·V, so those rows stay finite and exact."""
+    ins = synth.sdpa_inputs(47, 1, 2, 200, 200, 64, dtype="bf16")
+    Vst = ins["V"][0].copy()
+    Vst.view(np.uint16)[:, :, 160:] = 0x7fc0  # bf16 NaN
+    tq, tk = (to_dev(ins[n][0], "bf16") for n in "QK")
+    tv = to_dev(Vst, "bf16")
+    note("sdpa bf16 causal [1,2,200,200] NaN values past row 159")
+    out = libmha.sdpa(tq, tk, tv, scale=0.125, mask="causal")
+    torch.cuda.synchronize()
+    got = from_dev(out)[:, :, :160]
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], 0.125, oracle.MASK_CAUSAL)[:, :, :160]
+    _check(got, exp, "bf16", "causal rows < 160 with NaN values past them")
+
+
 def test_workload_decode_step():
     """The decoding-step workload (64 beams, h 8, one query row against a
     2048-entry cache with lengths in [1792, 2048]), all outputs."""

@@ -1,0 +1,121 @@
+"""Restricted attention (mha_sdpa_window) on the GPU against the fp64 oracle.
+
+Key c is visible to query r iff r - left <= c <= r + right (nickwang.xyz
+§4, Table 1: attention restricted to a neighbourhood of the output
+position).  Tolerance as for mha_sdpa: max-abs 2e-2 (bf16/fp16), 1e-5
+(fp32).  The window pins of ``tests/pins.py`` re-run through the API; the
+parity cases span several query blocks and key tiles with ragged tails,
+windows narrower and wider than a tile, one-sided windows, key padding,
+n_q != n_k, every head dimension and one-, two- and four-wave workgroups.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import TOL, from_dev, gpu_sdpa, gpu_sdpa_window, lens_dev, note, require_gpu, to_dev, torch
+import pins
+from transformer_head_scaled_amd import libmha, synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _check(got, exp, dtype, what):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(got - exp))) if got.size else 0.0
+    print(f"[parity] {what}: max-abs {err:.3e} (tol {TOL[dtype]:.0e})", flush=True)
+    assert err <= TOL[dtype], f"{what}: max-abs {err:.3e} > {TOL[dtype]}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("pin", pins.WINDOW_PINS, ids=lambda p: p.__name__)
+def test_window_pin_through_api(pin, dtype):
+    import inspect
+    note(f"window {dtype} {pin.__name__}")
+    wfn = gpu_sdpa_window(dtype)
+    if "sdpa_fn" in inspect.signature(pin).parameters:
+        pin(wfn, gpu_sdpa(dtype)[0], atol=TOL[dtype])
+    else:
+        pin(wfn, atol=TOL[dtype])
+
+
+def _run(ins, dtype, left, right, lens=None, scale=0.125):
+    tq, tk, tv = (to_dev(ins[n][0], dtype) for n in "QKV")
+    out = libmha.sdpa_window(tq, tk, tv, left, right, scale=scale, seq_lens=lens_dev(lens))
+    torch.cuda.synchronize()
+    return from_dev(out)
+
+
+CASES = [
+    # (B, h, n_q, n_k, left, right, lens)
+    (2, 2, 300, 300, 0, 0, None),            # each row sees itself only
+    (2, 2, 300, 300, 1, 1, [300, 130]),      # narrow, key padding
+    (1, 3, 517, 517, 63, 63, None),          # edges inside a 64-key tile
+    (1, 2, 517, 517, 64, 64, None),          # edges on tile boundaries
+    (2, 2, 450, 450, 100, 37, [450, 7]),     # lopsided, a very short batch
+    (1, 2, 400, 400, 0, 200, None),          # forward-looking only
+    (1, 2, 400, 400, 150, 0, None),          # causal band (not routed to the causal kernel)
+    (2, 1, 260, 700, 255, 255, [700, 500]),  # n_q < n_k
+    (1, 2, 700, 260, 30, 90, None),          # n_q > n_k: late rows see no key
+    (1, 2, 33, 1000, 5, 5, None),            # one-wave workgroups (n_q <= 64)
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c[:4])) + f"_w{c[4]}-{c[5]}"
+                         + ("_lens" if c[6] else ""))
+def test_window_parity(dtype, case):
+    B, h, n_q, n_k, left, right, lens = case
+    ins = synth.sdpa_inputs(800 + n_q + left, B, h, n_q, n_k, 64, dtype=dtype)
+    note(f"window {dtype} {case}")
+    got = _run(ins, dtype, left, right, lens)
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], 0.125, oracle.MASK_NONE, lens,
+                      window=(left, right))
+    _check(got, exp, dtype, f"window {dtype} {case}")
+
+
+@pytest.mark.parametrize("d", [16, 32, 128])
+def test_window_head_dims(d):
+    ins = synth.sdpa_inputs(850 + d, 2, 2, 390, 390, d, dtype="bf16")
+    note(f"window bf16 d={d}")
+    got = _run(ins, "bf16", 70, 20, [390, 200], scale=1 / math.sqrt(d))
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], 1 / math.sqrt(d), oracle.MASK_NONE,
+                      [390, 200], window=(70, 20))
+    _check(got, exp, "bf16", f"window d={d}")
+
+
+@pytest.mark.parametrize("left,right", [(128, 128), (300, 0), (0, 0), (2000, 2000)])
+def test_window_four_wave(left, right):
+    """[8,16,1000,1000] bf16: four-wave workgroups; one whole head per batch."""
+    lens = [1000, 999, 500, 64, 63, 1, 0, 1100]
+    ins = synth.sdpa_inputs(870 + left, 8, 16, 1000, 1000, 64, dtype="bf16")
+    note(f"window bf16 [8,16,1000,1000] ({left},{right})")
+    got = _run(ins, "bf16", left, right, lens)
+    Q, K, V = (ins[n][1] for n in "QKV")
+    for b in range(8):
+        i = (5 * b + 3) % 16
+        exp = oracle.sdpa(Q[b:b + 1, i:i + 1], K[b:b + 1, i:i + 1], V[b:b + 1, i:i + 1], 0.125,
+                          oracle.MASK_NONE, [lens[b]], window=(left, right))[0, 0]
+        _check(got[b, i], exp, "bf16", f"window ({left},{right}) head ({b},{i}) len {lens[b]}")
+
+
+def test_window_routes_match_plain_and_causal():
+    """Windows that reach every key, or every earlier key and no later one,
+    run the unmasked and causal kernels: bitwise the mha_sdpa results."""
+    ins = synth.sdpa_inputs(890, 2, 4, 600, 600, 64, dtype="bf16")
+    tq, tk, tv = (to_dev(ins[n][0], "bf16") for n in "QKV")
+    note("window routes")
+    full = libmha.sdpa_window(tq, tk, tv, 600, 600, scale=0.125)
+    causal_w = libmha.sdpa_window(tq, tk, tv, 599, 0, scale=0.125)
+    plain = libmha.sdpa(tq, tk, tv, scale=0.125, mask="none")
+    causal = libmha.sdpa(tq, tk, tv, scale=0.125, mask="causal")
+    torch.cuda.synchronize()
+    assert torch.equal(full, plain)
+    assert torch.equal(causal_w, causal)

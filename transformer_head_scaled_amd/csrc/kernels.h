@@ -21,9 +21,15 @@ struct SdpaArgs {
   float c;              // max(|scale| * log2(e), 1e-30)   (MFMA path)
   int32_t neg;          // scale < 0: the MFMA path negates Q exactly
   const int32_t* lens;  // device int32[B] valid key counts, or null
+  // restricted attention: key c visible to query r iff
+  // r - win_left <= c <= r + win_right (window != 0; reaches clamped to
+  // [0, n_q] and [0, n_k])
+  int32_t window, win_left, win_right;
 };
 
 hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float scale, hipStream_t st);
+// the flash kernel's window form (bf16 / fp16), sdpa_window.hip
+hipError_t launch_sdpa_window(const SdpaArgs& a, int dtype, int d, hipStream_t st);
 int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t n_k, int64_t heads);
 
 // One GEMM C = A·W of the projections: A [M, K] row-major (row stride lda),

@@ -113,43 +113,56 @@ const char* mha_last_error(void) { return g_err; }
 
 int mha_version(void) { return 200; }
 
-int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype, int64_t B,
-             int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, float scale,
-             int32_t mask_kind, const int32_t* seq_lens, void* stream) {
+// mha_sdpa and mha_sdpa_window: with `window`, key c is visible to query r
+// iff r - left <= c <= r + right.
+static int sdpa_impl(const char* fn, const void* Q, const void* K, const void* V, void* O,
+                     int32_t dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k,
+                     int64_t d_v, float scale, int32_t mask_kind, bool window, int64_t left,
+                     int64_t right, const int32_t* seq_lens, void* stream) {
   if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16)
-    return fail(MHA_ERR_DTYPE, "mha_sdpa: dtype %d", (int)dtype);
+    return fail(MHA_ERR_DTYPE, "%s: dtype %d", fn, (int)dtype);
   if (mask_kind != MHA_MASK_NONE && mask_kind != MHA_MASK_CAUSAL)
-    return fail(MHA_ERR_INVALID_ARG, "mha_sdpa: mask_kind %d", (int)mask_kind);
+    return fail(MHA_ERR_INVALID_ARG, "%s: mask_kind %d", fn, (int)mask_kind);
   if (B < 0 || h < 0 || n_q < 0 || n_k < 0 || d_k <= 0 || d_v <= 0)
-    return fail(MHA_ERR_SHAPE, "mha_sdpa: negative or zero size");
+    return fail(MHA_ERR_SHAPE, "%s: negative or zero size", fn);
   if (n_q > kMaxRows || n_k > kMaxRows || B > 65535 || h > 65535 || B * h > (int64_t)1 << 24)
-    return fail(MHA_ERR_SHAPE, "mha_sdpa: size beyond the supported range");
+    return fail(MHA_ERR_SHAPE, "%s: size beyond the supported range", fn);
   if (mask_kind == MHA_MASK_CAUSAL && n_q != n_k)
-    return fail(MHA_ERR_SHAPE, "mha_sdpa: causal mask needs n_q == n_k (%lld vs %lld)",
+    return fail(MHA_ERR_SHAPE, "%s: causal mask needs n_q == n_k (%lld vs %lld)", fn,
                 (long long)n_q, (long long)n_k);
-  if (!std::isfinite(scale)) return fail(MHA_ERR_INVALID_ARG, "mha_sdpa: scale is not finite");
+  if (!std::isfinite(scale)) return fail(MHA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (window && (left < 0 || right < 0))
+    return fail(MHA_ERR_INVALID_ARG, "%s: window reaches must be >= 0 (%lld, %lld)", fn,
+                (long long)left, (long long)right);
+  // a window that reaches every key is no restriction; one that reaches every
+  // earlier key and no later one is the causal mask
+  if (window && left >= n_q - 1 && right >= n_k - 1) window = false;
+  if (window && left >= n_q - 1 && right == 0 && n_q == n_k) {
+    window = false;
+    mask_kind = MHA_MASK_CAUSAL;
+  }
   if (dtype == MHA_F32) {
     if (d_k != d_v || (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128))
-      return fail(MHA_ERR_UNSUPPORTED, "mha_sdpa: f32 needs d_k == d_v in {16,32,64,128}");
+      return fail(MHA_ERR_UNSUPPORTED, "%s: f32 needs d_k == d_v in {16,32,64,128}", fn);
   } else if (d_k != d_v || (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128)) {
-    return fail(MHA_ERR_UNSUPPORTED, "mha_sdpa: bf16/f16 needs d_k == d_v in {16,32,64,128}");
+    return fail(MHA_ERR_UNSUPPORTED, "%s: bf16/f16 needs d_k == d_v in {16,32,64,128}", fn);
   } else if (n_k * d_k * 2 > kMaxBufferBytes) {
-    return fail(MHA_ERR_UNSUPPORTED, "mha_sdpa: one head's K/V exceeds 2 GiB (n_k %lld)",
+    return fail(MHA_ERR_UNSUPPORTED, "%s: one head's K/V exceeds 2 GiB (n_k %lld)", fn,
                 (long long)n_k);
   }
   if (B == 0 || h == 0 || n_q == 0) return ok();
   if (!Q || !O || ((!K || !V) && n_k > 0))
-    return fail(MHA_ERR_INVALID_ARG, "mha_sdpa: null tensor pointer");
+    return fail(MHA_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3) != 0)
-    return fail(MHA_ERR_INVALID_ARG, "mha_sdpa: tensors must be 16-byte aligned");
+    return fail(MHA_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
   const size_t es = elem_size(dtype);
   const Range ro = range_of(O, (size_t)(B * h * n_q * d_v) * es);
   if (overlap(ro, range_of(Q, (size_t)(B * h * n_q * d_k) * es)) ||
       overlap(ro, range_of(K, (size_t)(B * h * n_k * d_k) * es)) ||
       overlap(ro, range_of(V, (size_t)(B * h * n_k * d_v) * es)) ||
       (seq_lens && overlap(ro, range_of(seq_lens, (size_t)B * 4))))
-    return fail(MHA_ERR_ALIAS, "mha_sdpa: O overlaps an input");
+    return fail(MHA_ERR_ALIAS, "%s: O overlaps an input", fn);
 
   mha::SdpaArgs a{};
   a.Q = Q;
@@ -167,20 +180,47 @@ int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype
   a.c = std::fmax(std::fabs(scale) * 1.4426950408889634f, 1e-30f);
   a.neg = scale < 0.f ? 1 : 0;
   a.lens = seq_lens;
+  a.window = window ? 1 : 0;
+  a.win_left = (int32_t)(left < n_q ? left : n_q);
+  a.win_right = (int32_t)(right < n_k ? right : n_k);
   if (trace_on()) {
-    const double vis = mask_kind == MHA_MASK_CAUSAL ? 0.5 * n_q * (n_q + 1) : (double)n_q * n_k;
+    double vis = mask_kind == MHA_MASK_CAUSAL ? 0.5 * n_q * (n_q + 1) : (double)n_q * n_k;
+    if (window) {
+      vis = 0.0;
+      for (int64_t r = 0; r < n_q; ++r) {
+        const int64_t lo = r - a.win_left > 0 ? r - a.win_left : 0;
+        const int64_t hi = r + a.win_right < n_k - 1 ? r + a.win_right : n_k - 1;
+        if (hi >= lo) vis += (double)(hi - lo + 1);
+      }
+    }
     std::fprintf(stderr,
-                 "[libmha] sdpa dtype=%d B=%lld h=%lld n_q=%lld n_k=%lld d=%lld mask=%d lens=%s "
-                 "rows/wg=%d flops(dense-visible)=%.4g bytes=%.4g\n",
-                 (int)dtype, (long long)B, (long long)h, (long long)n_q, (long long)n_k,
-                 (long long)d_k, (int)mask_kind, seq_lens ? "yes" : "no",
+                 "[libmha] %s dtype=%d B=%lld h=%lld n_q=%lld n_k=%lld d=%lld mask=%d window=%d,%d "
+                 "lens=%s rows/wg=%d flops(visible)=%.4g bytes=%.4g\n",
+                 fn, (int)dtype, (long long)B, (long long)h, (long long)n_q, (long long)n_k,
+                 (long long)d_k, (int)mask_kind, window ? a.win_left : -1, window ? a.win_right : -1,
+                 seq_lens ? "yes" : "no",
                  mha::sdpa_rows_per_workgroup(dtype, mask_kind == MHA_MASK_CAUSAL, n_q, n_k, B * h), 4.0 * d_k * vis * B * h,
                  (double)es * B * h * (2 * n_q * d_k + 2 * n_k * d_k));
   }
   const hipError_t e = mha::launch_sdpa(a, dtype, mask_kind == MHA_MASK_CAUSAL, (int)d_k, scale,
                                         (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "mha_sdpa launch");
+  if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
+}
+
+int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype, int64_t B,
+             int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, float scale,
+             int32_t mask_kind, const int32_t* seq_lens, void* stream) {
+  return sdpa_impl("mha_sdpa", Q, K, V, O, dtype, B, h, n_q, n_k, d_k, d_v, scale, mask_kind,
+                   false, 0, 0, seq_lens, stream);
+}
+
+int mha_sdpa_window(const void* Q, const void* K, const void* V, void* O, int32_t dtype,
+                    int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v,
+                    float scale, int64_t left, int64_t right, const int32_t* seq_lens,
+                    void* stream) {
+  return sdpa_impl("mha_sdpa_window", Q, K, V, O, dtype, B, h, n_q, n_k, d_k, d_v, scale,
+                   MHA_MASK_NONE, true, left, right, seq_lens, stream);
 }
 
 size_t mha_forward_workspace_size(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model,

@@ -25,7 +25,7 @@ MHA_ERR_ALIAS = -6
 MHA_ERR_HIP = -7
 
 # every symbol include/mha.h declares
-EXPORTS = ("mha_sdpa", "mha_forward", "mha_forward_workspace_size", "mha_add_norm",
+EXPORTS = ("mha_sdpa", "mha_sdpa_window", "mha_forward", "mha_forward_workspace_size", "mha_add_norm",
            "mha_forward_add_norm", "mha_forward_add_norm_workspace_size", "mha_status_string",
            "mha_last_error", "mha_version")
 
@@ -50,6 +50,9 @@ def lib():
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     L.mha_sdpa.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, f32, i32, vp, vp]
     L.mha_sdpa.restype = ctypes.c_int
+    L.mha_sdpa_window.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, f32, i64, i64,
+                                  vp, vp]
+    L.mha_sdpa_window.restype = ctypes.c_int
     L.mha_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32, i32, vp,
                               vp, ctypes.c_size_t, vp]
     L.mha_forward.restype = ctypes.c_int
@@ -149,6 +152,28 @@ def sdpa(Q, K, V, scale=None, mask="none", seq_lens=None, out=None, stream=None)
     lens = _lens(seq_lens, B, "seq_lens")
     _check(lib().mha_sdpa(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), dtype_code(Q), B, h, n_q, n_k,
                           d_k, d_v, float(scale), _mask_code(mask), _ptr(lens), _stream(stream)))
+    return out
+
+
+def sdpa_window(Q, K, V, left, right, scale=None, seq_lens=None, out=None, stream=None):
+    """mha_sdpa_window: restricted attention, key c visible to query r iff
+    r - left <= c <= r + right.  Shapes as sdpa()."""
+    import torch
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _contig(t, n)
+        if t.dim() != 4:
+            raise ValueError(f"{n} must be 4-d [B, h, n, d]")
+    B, h, n_q, d_k = Q.shape
+    n_k, d_v = K.shape[2], V.shape[3]
+    if scale is None:
+        scale = 1.0 / float(d_k) ** 0.5
+    if out is None:
+        out = torch.empty((B, h, n_q, d_v), dtype=Q.dtype, device=Q.device)
+    _contig(out, "out")
+    lens = _lens(seq_lens, B, "seq_lens")
+    _check(lib().mha_sdpa_window(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), dtype_code(Q), B, h, n_q,
+                                 n_k, d_k, d_v, float(scale), int(left), int(right), _ptr(lens),
+                                 _stream(stream)))
     return out
 
 
