@@ -29,7 +29,10 @@ PEAK_HBM_GBS = 8000.0
 WORKLOAD = dict(B=4, h=8, n=4096, d=64)
 COPY_BYTES = 512 << 20   # plain device copy used to calibrate the HBM byte counters
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sdpa_fwd_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "transformer_head_scaled_amd", "csrc", "sdpa_fwd.hip")
+# the sources the attention kernel is compiled from (the traffic record is
+# tied to their hash)
+KERNEL_SRCS = [os.path.join(ROOT, "transformer_head_scaled_amd", "csrc", f)
+               for f in ("sdpa_fwd_kernel.h", "sdpa_fwd.hip", "device_common.h")]
 
 
 def sdpa_flops(B, h, n_q, n_k, d, causal):
@@ -38,8 +41,11 @@ def sdpa_flops(B, h, n_q, n_k, d, causal):
 
 
 def kernel_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -96,7 +102,8 @@ def other_configs(dev, stream, iters=100):
     attention with key padding (B 32, n 64, d_model 512, h 8), causal SDPA
     (B 16, h 8, n 512), mha_forward cross attention (B 8, n_q 384, n_k 512,
     d_model 1024, h 16) also with its Add & Norm, the Add & Norm alone on
-    those rows, and one decoding step (B 64, h 8, one query row against a
+    those rows, restricted attention on the long-sequence batch (a window
+    of 513 keys), and one decoding step (B 64, h 8, one query row against a
     2048-entry key/value cache, HBM-bound).  Rates use algorithmic
     flops and bytes.  Cold calls follow a read of a 512 MB buffer (a read
     leaves clean lines; an overwrite would leave dirty ones that the timed
@@ -194,6 +201,30 @@ def other_configs(dev, stream, iters=100):
                       "gbs_cold": round(nbytes / (cmed * 1e-6) / 1e9, 1),
                       "hbm_frac_cold": round(nbytes / (cmed * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                       "flops": fl, "bytes": nbytes}
+    # restricted self-attention on the long-sequence workload: a centred
+    # neighbourhood of 513 keys (reach 256 on each side); flops on the
+    # visible pairs only
+    w5 = synth.WORKLOADS[5]
+    ins5 = synth.sdpa_inputs(5, w5["B"], w5["h"], w5["n_q"], w5["n_k"], w5["d"], dtype="bf16")
+    Q5, K5, V5 = (dev_t(ins5[k][0]) for k in "QKV")
+    O5 = torch.empty_like(Q5)
+    reach = 256
+
+    def call_w():
+        libmha.sdpa_window(Q5, K5, V5, reach, reach, scale=0.125, out=O5, stream=stream)
+    for _ in range(20):
+        call_w()
+    med, mn = time_calls(call_w, stream, iters)
+    n5 = w5["n_q"]
+    r = np.arange(n5)
+    pairs = float(np.sum(np.minimum(n5 - 1, r + reach) - np.maximum(0, r - reach) + 1))
+    fl = 4.0 * w5["d"] * pairs * w5["B"] * w5["h"]
+    res["sdpa_window_bf16_b4_h8_n4096_d64_reach256"] = {
+        "call": "mha_sdpa_window", "us_median": round(med, 2), "us_min": round(mn, 2),
+        "tflops": round(fl / (med * 1e-6) / 1e12, 2),
+        "pct_peak": round(100 * fl / (med * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2), "flops": fl}
+    del Q5, K5, V5, O5
+
     # decoding step: bytes = the visible K and V rows + Q + O
     w = synth.WORKLOADS[6]
     ins, lens = synth.workload_inputs(6)

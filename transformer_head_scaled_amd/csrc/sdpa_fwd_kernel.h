@@ -275,7 +275,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   // issue this wave's two LDS-destination loads of K (or V) for one tile.
   // The K and V halves are issued at different points of a step, so that
   // the waves of a compute unit do not all queue their loads at once.
-  auto gload_k = [&](int tile, int stage) {
+  auto gload_k = [&](int tile, int stage) __attribute__((always_inline)) {
     if (!loader) return;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
                     k_lane[i % NKL] + (uint32_t)(r * KPP * p.k_sr * 2) + tile * k_tile);
     }
   };
-  auto gload_v = [&](int tile, int stage) {
+  auto gload_v = [&](int tile, int stage) __attribute__((always_inline)) {
     if (!loader) return;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   // K fragment (kb, st) of this lane: key kb·32 + l32, chunk 2·st + hi
   // (kb·32 is a multiple of 128 / D, so the permutation is that of l32)
   const int kx = kswz<D>(l32);
-  auto kfrag = [&](int buf, int kb, int st) {
+  auto kfrag = [&](int buf, int kb, int st) __attribute__((always_inline)) {
     return *(const u32x4*)&Ks[kvw][buf][(kb * 32 + l32) * D + (((2 * st + hi) ^ kx) * 8)];
   };
   // Vᵀ fragment (kb, t2, db): d = db·32 + l32 and the 8 keys that the score
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   const int v_key_l = (4 * hi + (i16 >> 2)) ^ (v_pad ? 4 : 0);  // key offset within a 16-key step (+ 8·e)
   const int v_x = vswz<D>(v_key_l);  // the row permutation (the step starts at a multiple of 8)
   const int v_col = (D < 32 ? 0 : 16 * ((lane >> 4) & 1)) + 4 * (i16 & 3);  // d within the 32-column block
-  auto vfrag = [&](int buf, int kb, int t2, int db) {
+  auto vfrag = [&](int buf, int kb, int t2, int db) __attribute__((always_inline)) {
     u32x4 r;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   // Zero the Vᵀ fragment values of keys outside [vlo, vhi).  Element j of a
   // fragment holds key 4·hi + (j & 3) + 8·(j >> 2) of its 16-key step; dword
   // w holds elements 2w (low half) and 2w + 1.
-  auto zero_unseen_v = [&](u32x4 (&vf)[2][2][NDB], int kbase) {
+  auto zero_unseen_v = [&](u32x4 (&vf)[2][2][NDB], int kbase) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   // The row sum adds the fp32 weights with plain adds: a packed dot2 would
   // be exact to the rounded P, but on gfx950 it does not issue alongside
   // the matrix cores, while adds do.
-  auto weights = [&](int qi, int kb, const f32x16& sv, uint32_t (&pw)[8]) {
+  auto weights = [&](int qi, int kb, const f32x16& sv, uint32_t (&pw)[8]) __attribute__((always_inline)) {
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   };
   // per-element mask of query block qi (diagonal and key-length boundary
   // tiles only)
-  auto apply_mask = [&](int qi, int kbase, int kb, f32x16& sv) {
+  auto apply_mask = [&](int qi, int kbase, int kb, f32x16& sv) __attribute__((always_inline)) {
     const int row = row0[qi] + l32;
     if constexpr (WINDOW) {
       // visible iff lo <= the register's key offset in the tile < lim
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   };
   // Sᵀ of query block qi, key block kb, for the keys of LDS stage buf,
   // masked like the tile
-  auto scores = [&](auto masked, int qi, int buf, int kbase, int kb) {
+  auto scores = [&](auto masked, int qi, int buf, int kbase, int kb) __attribute__((always_inline)) {
     f32x16 sv = {};
 #pragma unroll
     for (int st = 0; st < NST; ++st) sv = mfma_32x32x16<DT>(kfrag(buf, kb, st), qf[qi][st], sv);
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   // exact path recomputes the scores from LDS (twice, one key block at a
   // time) instead of keeping them, which keeps the common path's register
   // footprint small.
-  auto settle = [&](auto masked, int qi, int buf, int kbase, uint32_t (&pw)[2][8], float rs) {
+  auto settle = [&](auto masked, int qi, int buf, int kbase, uint32_t (&pw)[2][8], float rs) __attribute__((always_inline)) {
     // `!(rs <= kAccept)` is also true for NaN
     const bool reject = (m[qi] == -INFINITY) || !(rs <= kAccept);
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(reject) != 0, 0)) {
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   // instructions of the other:
   //   S0 (MFMA), then S1 (MFMA) interleaved with the weights of block 0,
   //   P0·V (MFMA) interleaved with the weights of block 1, then P1·V.
-  auto tile = [&](auto masked, int buf, int kbase, auto&& mid) {
+  auto tile = [&](auto masked, int buf, int kbase, auto&& mid) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     u32x4 kf[2][NST];
 #pragma unroll
@@ -554,7 +554,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
 
   // One 64-key tile for block 1 only (causal: block 0 has no visible key
   // left).
-  auto tile_hi = [&](auto masked, int buf, int kbase, auto&& mid) {
+  auto tile_hi = [&](auto masked, int buf, int kbase, auto&& mid) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     f32x16 s1[2];
 #pragma unroll
@@ -590,12 +590,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   // One step of the key loop: start the loads of tile j + NSTAGE - 1,
   // compute tile j (both blocks, block 1 only, or nothing), barrier.
   // WHAT: 0 = nothing, 1 = block 1 only, 2 = both blocks.
-  auto step = [&](int j, auto masked, auto what) {
+  auto step = [&](int j, auto masked, auto what) __attribute__((always_inline)) {
     constexpr int WHAT = decltype(what)::value;
     const int buf = j % NSTAGE;
     const bool more = j + NSTAGE - 1 < ntiles;
     if (more) gload_k(j + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE);
-    auto load_v = [&]() {
+    auto load_v = [&]() __attribute__((always_inline)) {
       if (more) gload_v(j + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE);
     };
     const int kbase = j * BN;
@@ -650,12 +650,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
     // tile t + NSTAGE − 1 go out at the top of step t (K) and mid-tile (V)
     // into the stage that step t − 1 read; the step ends with this wave's
     // own wait for tile t + 1 (no barrier)
-    auto split_step = [&](int t, auto masked) {
+    auto split_step = [&](int t, auto masked) __attribute__((always_inline)) {
       const int jt = wave + t * NW;
       const int ta = t + NSTAGE - 1;
       const bool more = ta < myn;
       if (more) gload_k(wave + ta * NW, ta % NSTAGE);
-      auto load_v = [&]() {
+      auto load_v = [&]() __attribute__((always_inline)) {
         if (more) gload_v(wave + ta * NW, ta % NSTAGE);
       };
       tile_hi(masked, t % NSTAGE, jt * BN, load_v);

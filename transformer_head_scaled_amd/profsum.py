@@ -21,13 +21,18 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SRC = os.path.join(ROOT, "transformer_head_scaled_amd", "csrc", "sdpa_fwd.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "transformer_head_scaled_amd", "csrc", f)
+               for f in ("sdpa_fwd_kernel.h", "sdpa_fwd.hip", "device_common.h")]
 COPY_BYTES = 512 << 20
 
 
 def kernel_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the attention kernel's sources (the same as bench.py's)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_stats(path):
