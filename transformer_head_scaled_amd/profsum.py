@@ -18,6 +18,7 @@ import collections
 import hashlib
 import json
 import os
+import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -88,10 +89,17 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json, commands):
         wb = w.get(name, 0.0) * 1024.0 * write_factor
         res["kernels"][name] = {"fetch_kib": f[name], "write_kib": w.get(name),
                                 "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
-    # the bench workload is the largest launch of each mode (smaller SDPA
-    # launches of other workloads may be in the same run)
-    for mode, tag in (("noncausal", ", false,"), ("causal", ", true,")):
-        cands = [v["bytes_per_launch"] for k, v in res["kernels"].items() if tag in k]
+    # the bench workload is the largest launch of each mode among the plain
+    # d = 64 kernels (template arguments: dtype, d, causal, waves, key split,
+    # window); smaller launches of other workloads may be in the same run
+    targs = re.compile(r"sdpa_fwd_kernel<(\d+), (\d+), (true|false), (\d+), (true|false), (true|false)>")
+    for mode, causal in (("noncausal", "false"), ("causal", "true")):
+        cands = []
+        for k, v in res["kernels"].items():
+            m = targs.search(k)
+            if m and m.group(2) == "64" and m.group(3) == causal and m.group(5) == "false" \
+                    and m.group(6) == "false":
+                cands.append(v["bytes_per_launch"])
         if cands:
             res[mode + "_bytes_per_launch"] = max(cands)
     with open(out_json, "w") as fh:
