@@ -132,14 +132,53 @@ hipError_t launch_nw(const SdpaArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The causal pair layout (sdpa_fwd_kernel.h): a workgroup of NW waves takes
+// NW consecutive 32-row blocks.  It is the causal layout for d >= 64
+// (measured 0-3 % faster than two blocks u, nb − 1 − u per wave at d = 64,
+// 28 % at d = 128); at d = 16, 32, where the exponentials bound the kernel,
+// the other measured 5-10 % faster and is kept.  0 selects the other for all.
+#ifndef SDPA_CAUSAL_PAIRS
+#define SDPA_CAUSAL_PAIRS 1
+#endif
+template <int DT, int DH, int NW>
+hipError_t launch_pairs_nw(const SdpaArgs& a, hipStream_t st) {
+  const int64_t grid = (a.n_q + NW * 32 - 1) / (NW * 32) * a.B * a.H;
+  hipLaunchKernelGGL((sdpa_fwd_kernel<DT, DH, true, NW, false, false, true>), dim3((unsigned)grid),
+                     dim3(NW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+// Waves per pair workgroup: eight (each loaded tile then serves 256 query
+// rows, as in the other layouts; measured faster than four), four for
+// d = 128 (one wave per SIMD) and short sequences, fewer below 64 rows.
+int pairs_waves(int64_t n_q, int d) {
+  if (n_q <= 32) return 1;
+  if (n_q <= 64) return 2;
+  return (d <= 64 && n_q > 128) ? 8 : 4;
+}
+
+template <int DT, int DH>
+hipError_t launch_pairs(const SdpaArgs& a, hipStream_t st) {
+  switch (pairs_waves(a.n_q, DH)) {
+    case 1: return launch_pairs_nw<DT, DH, 1>(a, st);
+    case 2: return launch_pairs_nw<DT, DH, 2>(a, st);
+    case 4: return launch_pairs_nw<DT, DH, 4>(a, st);
+    default: return launch_pairs_nw<DT, DH, (DH <= 64 ? 8 : 4)>(a, st);
+  }
+}
+
 template <int DT, int DH, bool CAUSAL>
 hipError_t launch_mfma(const SdpaArgs& a, hipStream_t st) {
-  if (use_split(a.n_q, a.n_k, (int64_t)a.B * a.H, CAUSAL))
-    return launch_split<DT, DH, split_waves(DH)>(a, st);
-  switch (waves_per_wg(a.n_q, (int64_t)a.B * a.H, CAUSAL)) {
-    case 1: return launch_nw<DT, DH, CAUSAL, 1>(a, st);
-    case 2: return launch_nw<DT, DH, CAUSAL, 2>(a, st);
-    default: return launch_nw<DT, DH, CAUSAL, 4>(a, st);
+  if constexpr (CAUSAL && SDPA_CAUSAL_PAIRS && DH >= 64) {
+    return launch_pairs<DT, DH>(a, st);
+  } else {
+    if (use_split(a.n_q, a.n_k, (int64_t)a.B * a.H, CAUSAL))
+      return launch_split<DT, DH, split_waves(DH)>(a, st);
+    switch (waves_per_wg(a.n_q, (int64_t)a.B * a.H, CAUSAL)) {
+      case 1: return launch_nw<DT, DH, CAUSAL, 1>(a, st);
+      case 2: return launch_nw<DT, DH, CAUSAL, 2>(a, st);
+      default: return launch_nw<DT, DH, CAUSAL, 4>(a, st);
+    }
   }
 }
 
@@ -170,6 +209,7 @@ hipError_t launch_f32(const SdpaArgs& a, float scale, int causal, hipStream_t st
 
 int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t n_k, int64_t heads) {
   if (dtype == DT_F32) return 64;
+  if (causal && SDPA_CAUSAL_PAIRS) return pairs_waves(n_q, 64) * 32;  // (d >= 64)
   if (use_split(n_q, n_k, heads, causal != 0)) return 32;
   return waves_per_wg(n_q, heads, causal != 0) * 64;
 }

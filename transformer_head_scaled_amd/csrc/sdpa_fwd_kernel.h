@@ -120,10 +120,18 @@ constexpr int split_waves(int d) {
 // tiles some of its rows can see, and each wave computes, per tile, nothing
 // (no row of its own sees a key there), the masked tile code (a window edge
 // crosses the tile) or the plain one (all its rows see the whole tile).
-template <int DT, int DH, bool CAUSAL, int NW, bool SPLIT = false, bool WINDOW = false>
+//
+// PAIRS (causal): one 32-row block per wave, consecutive blocks per
+// workgroup, and two consecutive key tiles per step, which take the places
+// of the two blocks of the default layout in the tile code (S of one tile
+// computed while the other's exponentials run).  Workgroups are launched
+// longest first (the work of a block grows with its rows).
+template <int DT, int DH, bool CAUSAL, int NW, bool SPLIT = false, bool WINDOW = false,
+          bool PAIRS = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 1 || DH > 64 || SPLIT) ? 1 : 2, 2))) void sdpa_fwd_kernel(SdpaArgs p) {
   static_assert(!(SPLIT && CAUSAL), "the key split is for the unmasked case");
   static_assert(!(WINDOW && (CAUSAL || SPLIT)), "the window has its own mask");
+  static_assert(!PAIRS || (CAUSAL && !SPLIT && !WINDOW), "the pair layout is a causal layout");
   constexpr int D = DH;
   constexpr int QB = 2, BN = 64, NSTAGE = SPLIT ? split_stages(DH) : 2;
   constexpr int BM = NW * 32 * QB;  // query rows per workgroup
@@ -135,15 +143,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   constexpr int CPW = PIECES >= NW ? PIECES / NW : 1;  // pieces loaded per (loading) wave
   constexpr int NKL = CR >= 8 ? CR / 4 : 1;  // distinct per-lane K offsets (by piece)
   static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head dimension");
-  static_assert(CPW % NKL == 0, "a wave's first piece must start a K offset cycle");
   constexpr float kAccept = 256.f;  // accept a tile while partial row sums are <= 2^8
   constexpr int NBUF = SPLIT ? NW : 1;  // LDS rings: one per wave with the key split
+  constexpr int NSLOT = PAIRS ? 2 : 1;  // tiles per ring stage
 
   // K tile: [key][D], rows of D / 8 16-byte chunks permuted by kswz
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF][NSTAGE][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF][NSTAGE * NSLOT][BN * D];
   // V tile: [key][D], chunks permuted by vswz, which keeps the transposing
   // fragment reads conflict-free
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[NBUF][NSTAGE][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NBUF][NSTAGE * NSLOT][BN * D];
 
   // Rows.  Unmasked: workgroup qb of a head takes rows [qb·BM, qb·BM + BM),
   // each wave 64 consecutive rows.  Causal: the work of a row grows with its
@@ -153,11 +161,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   // run side by side until the end, instead of a long wave finishing alone.
   const int nb32e = ((p.n_q + 31) / 32 + 1) & ~1;
   const int units = nb32e / 2;  // causal: waves of work per head
-  const int nqb = SPLIT ? (p.n_q + 31) / 32 : CAUSAL ? (units + NW - 1) / NW : (p.n_q + BM - 1) / BM;
+  const int nqb = PAIRS ? (p.n_q + NW * 32 - 1) / (NW * 32)
+                  : SPLIT ? (p.n_q + 31) / 32 : CAUSAL ? (units + NW - 1) / NW : (p.n_q + BM - 1) / BM;
   const uint32_t total = (uint32_t)nqb * p.B * p.H;
-  const uint32_t t = xcd_remap(blockIdx.x, total);
-  const int bh = t / nqb;
-  const int qb = t % nqb;
+  // pairs: consecutive workgroups are different heads at the same rows,
+  // highest rows (most work) first; they spread over the XCDs round-robin
+  // (grouping each head's workgroups on one XCD measured no faster)
+  const uint32_t t = PAIRS ? blockIdx.x : xcd_remap(blockIdx.x, total);
+  const uint32_t nbh = (uint32_t)p.B * p.H;
+  const int bh = PAIRS ? (int)(t % nbh) : (int)(t / nqb);
+  const int qb = PAIRS ? nqb - 1 - (int)(t / nbh) : (int)(t % nqb);
   const int b = bh / p.H, hh = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is the same for all lanes of a wave: readfirstlane makes
@@ -168,9 +181,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   int n_eff = p.n_k;
   if (p.lens) n_eff = min(max(p.lens[b], 0), p.n_k);
   const int unit = qb * NW + wave;
-  const bool wave_active = !CAUSAL || unit < units;
+  const bool wave_active =
+      !CAUSAL || (PAIRS ? qb * NW * 32 + wave * 32 < p.n_q : unit < units);
   int row0[QB];  // first row of each of this wave's two 32-row blocks
-  if (CAUSAL) {
+  if (PAIRS) {
+    // one block per wave; the tile code of the upper block does the work
+    row0[0] = row0[1] = qb * NW * 32 + wave * 32;
+  } else if (CAUSAL) {
     row0[0] = 32 * unit;
     row0[1] = 32 * (nb32e - 1 - unit);
   } else if (SPLIT) {
@@ -183,7 +200,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   int kend = n_eff;
   // causal: keys up to the last row of the workgroup's first wave (its
   // upper block is the highest of the workgroup)
-  if (CAUSAL) kend = min(kend, 32 * (nb32e - qb * NW));
+  if (CAUSAL) kend = min(kend, PAIRS ? qb * NW * 32 + NW * 32 : 32 * (nb32e - qb * NW));
   // window: the keys the workgroup's first row reaches back to, up to those
   // its last row reaches forward to
   int jlo = 0;  // first key tile of the workgroup
@@ -267,6 +284,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   const uint32_t v_lane =
       (uint32_t)(((lane / CR) * p.v_sr + ((lane % CR) ^ vswz<D>(lane / CR)) * 8) * 2);
   const uint32_t k_tile = (uint32_t)(BN * p.k_sr * 2), v_tile = (uint32_t)(BN * p.v_sr * 2);
+  // the K offset of piece r for this lane: from the table when a wave's
+  // pieces start a cycle of NKL (CPW a multiple of NKL), else computed
+  auto k_lane_of = [&](int r, int i) __attribute__((always_inline)) {
+    if constexpr (SPLIT || CPW % NKL == 0) {
+      return k_lane[i % NKL];
+    } else {
+      const int key = KPP * r + lane / CR;  // this lane's key in the tile
+      return (uint32_t)(((lane / CR) * p.k_sr + ((lane % CR) ^ kswz<D>(key)) * 8) * 2);
+    }
+  };
   // with fewer pieces than waves (D = 16, four waves) the last waves load none
   const bool loader = SPLIT || PIECES >= NW || wave < PIECES;
   constexpr int LPW = SPLIT ? PIECES : CPW;  // pieces this wave loads per tile
@@ -284,7 +311,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
       load_lds_b128(krs,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
                         __attribute__((address_space(3))) void*)&Ks[kvw][stage][r * 512]),
-                    k_lane[i % NKL] + (uint32_t)(r * KPP * p.k_sr * 2) + tile * k_tile);
+                    k_lane_of(r, i) + (uint32_t)(r * KPP * p.k_sr * 2) + tile * k_tile);
     }
   };
   auto gload_v = [&](int tile, int stage) __attribute__((always_inline)) {
@@ -340,7 +367,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   constexpr int kSplitKeep = SPLIT ? (NSTAGE - 2) * 2 * LPW : 0;
   static_assert(kSplitKeep < 64, "vmcnt range");
   constexpr int kSplitWait = (kSplitKeep & 15) | ((kSplitKeep >> 4) << 14) | 0x0070;
-  if (SPLIT) {
+  if (PAIRS) {  // the first pair of tiles into the two slots of stage 0
+    if (ntiles > 0) {
+      gload_k(0, 0);
+      gload_v(0, 0);
+    }
+    if (ntiles > 1) {
+      gload_k(1, 1);
+      gload_v(1, 1);
+    }
+  } else if (SPLIT) {
 #pragma unroll
     for (int t0 = 0; t0 < NSTAGE - 1; ++t0)  // this wave's first tiles
       if (t0 < myn) {
@@ -587,6 +623,122 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
         }
   };
 
+  // Two consecutive 64-key tiles (LDS buffers bufA and bufA + 1) for block 1
+  // alone, the pair layout.  The instruction order is that of `tile`, the
+  // tiles in the places of the blocks: S_A, then S_B interleaved with the
+  // weights of A; A is settled before B's weights are formed (both update
+  // the block's one softmax state); P_A·V interleaved with the weights of B,
+  // then P_B·V.
+  auto tile_pair = [&](auto masked, int bufA, int kbaseA, auto&& mid) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const int bufB = bufA + 1, kbaseB = kbaseA + BN;
+    u32x4 kf[2][NST];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < NST; ++st) kf[kb][st] = kfrag(bufA, kb, st);
+    f32x16 sa[2], sb[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+        sa[kb] = mfma_32x32x16<DT>(kf[kb][st], qf[1][st], st == 0 ? f32x16{} : sa[kb]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < NST; ++st) kf[kb][st] = kfrag(bufB, kb, st);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+        sb[kb] = mfma_32x32x16<DT>(kf[kb][st], qf[1][st], st == 0 ? f32x16{} : sb[kb]);
+    if constexpr (MASKED) {
+      apply_mask(1, kbaseA, 0, sa[0]);
+      apply_mask(1, kbaseA, 1, sa[1]);
+    }
+    uint32_t pa[2][8], pb[2][8];
+    const float rsa = weights(1, 0, sa[0], pa[0]) + weights(1, 1, sa[1], pa[1]);
+#pragma unroll
+    for (int g = 0; g < 2 * NST; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 112 / (2 * NST), 0);
+    }
+    u32x4 vf[2][2][NDB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          vf[kb][t2][db] = vfrag(bufA, kb, t2, db);
+    if constexpr (MASKED) zero_unseen_v(vf, kbaseA);
+    settle(masked, 1, bufA, kbaseA, pa, rsa);
+    mid();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const u32x4 bv = {pa[kb][4 * t2], pa[kb][4 * t2 + 1], pa[kb][4 * t2 + 2], pa[kb][4 * t2 + 3]};
+          o[1][db] = mfma_32x32x16<DT>(vf[kb][t2][db], bv, o[1][db]);
+        }
+    if constexpr (MASKED) {
+      apply_mask(1, kbaseB, 0, sb[0]);
+      apply_mask(1, kbaseB, 1, sb[1]);
+    }
+    const float rsb = weights(1, 0, sb[0], pb[0]) + weights(1, 1, sb[1], pb[1]);
+#pragma unroll
+    for (int g = 0; g < 4 * NDB; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 112 / (4 * NDB), 0);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          vf[kb][t2][db] = vfrag(bufB, kb, t2, db);
+    if constexpr (MASKED) zero_unseen_v(vf, kbaseB);
+    settle(masked, 1, bufB, kbaseB, pb, rsb);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const u32x4 bv = {pb[kb][4 * t2], pb[kb][4 * t2 + 1], pb[kb][4 * t2 + 2], pb[kb][4 * t2 + 3]};
+          o[1][db] = mfma_32x32x16<DT>(vf[kb][t2][db], bv, o[1][db]);
+        }
+  };
+
+  // One step of the pair layout: start the loads of the next pair (tiles
+  // 2s + 2, 2s + 3 into the other stage), compute this pair (both tiles,
+  // the first only, or nothing), wait, barrier.
+  auto pair_step = [&](int s, auto masked, auto what) __attribute__((always_inline)) {
+    constexpr int WHAT = decltype(what)::value;
+    const int nA = 2 * s + 2;
+    const bool moreA = nA < ntiles, moreB = nA + 1 < ntiles;
+    const int nbuf = 2 * ((s + 1) % NSTAGE);
+    if (moreA) gload_k(nA, nbuf);
+    if (moreB) gload_k(nA + 1, nbuf + 1);
+    auto load_v = [&]() __attribute__((always_inline)) {
+      if (moreA) gload_v(nA, nbuf);
+      if (moreB) gload_v(nA + 1, nbuf + 1);
+    };
+    const int buf = 2 * (s % NSTAGE), kbase = 2 * s * BN;
+    if constexpr (WHAT == 2)
+      tile_pair(masked, buf, kbase, load_v);
+    else if constexpr (WHAT == 1)
+      tile_hi(masked, buf, kbase, load_v);
+    else
+      load_v();
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the next pair has landed
+    asm volatile("s_barrier" ::: "memory");
+  };
+
   // One step of the key loop: start the loads of tile j + NSTAGE - 1,
   // compute tile j (both blocks, block 1 only, or nothing), barrier.
   // WHAT: 0 = nothing, 1 = block 1 only, 2 = both blocks.
@@ -621,7 +773,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   using yes = std::true_type;
   const int nfull = min(n_eff / BN, ntiles);  // tiles inside the valid keys
   int j = jlo;
-  if (WINDOW) {
+  if (PAIRS) {
+    // This wave's block [r0, r0 + 32): pairs with both tiles fully visible,
+    // then the pairs its diagonal (or the key length) crosses, masked, then
+    // nothing.  Every wave takes part in all S steps.
+    static_assert(NSTAGE == 2, "pair loads and waits assume two stages");
+    const int S = (ntiles + 1) / 2;
+    int s_full = 0, s_vis = 0, vis_end = 0;
+    if (wave_active) {
+      const int r0 = row0[1];
+      vis_end = min((r0 + 31) / BN + 1, (n_eff + BN - 1) / BN);  // past the last tile a row sees
+      const int unm_end = min((r0 + 1) / BN, n_eff / BN);         // tiles below: all rows see all keys
+      s_full = min(max(unm_end, 0) / 2, S);
+      s_vis = min(max((vis_end + 1) / 2, s_full), S);
+    }
+    int s = 0;
+    for (; s < s_full; ++s) pair_step(s, no{}, std::integral_constant<int, 2>{});
+    for (; s < s_vis; ++s) {
+      if (2 * s + 1 < vis_end)
+        pair_step(s, yes{}, std::integral_constant<int, 2>{});
+      else
+        pair_step(s, yes{}, std::integral_constant<int, 1>{});
+    }
+    for (; s < S; ++s) pair_step(s, no{}, std::integral_constant<int, 0>{});
+  } else if (WINDOW) {
     // This wave's phases over the workgroup's tiles [jlo, ntiles): nothing
     // up to a, masked up to ib, plain up to ie, masked up to z, nothing after.
     // Only its existing rows r0 .. rl count: rows past n_q are not stored.
@@ -735,7 +910,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
 
   // ---- normalise and store this lane's query row (4 consecutive d per store)
 #pragma unroll
-  for (int qi = SPLIT ? 1 : 0; qi < QB; ++qi) {
+  for (int qi = (SPLIT || PAIRS) ? 1 : 0; qi < QB; ++qi) {
     const float L = pair_sum(l[qi]);
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const int row = row0[qi] + l32;
