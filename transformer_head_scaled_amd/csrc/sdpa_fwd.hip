@@ -140,10 +140,10 @@ hipError_t launch_nw(const SdpaArgs& a, hipStream_t st) {
 #ifndef SDPA_CAUSAL_PAIRS
 #define SDPA_CAUSAL_PAIRS 1
 #endif
-template <int DT, int DH, int NW>
+template <int DT, int DH, bool CAUSAL, int NW>
 hipError_t launch_pairs_nw(const SdpaArgs& a, hipStream_t st) {
   const int64_t grid = (a.n_q + NW * 32 - 1) / (NW * 32) * a.B * a.H;
-  hipLaunchKernelGGL((sdpa_fwd_kernel<DT, DH, true, NW, false, false, true>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((sdpa_fwd_kernel<DT, DH, CAUSAL, NW, false, false, true>), dim3((unsigned)grid),
                      dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
@@ -157,20 +157,20 @@ int pairs_waves(int64_t n_q, int d) {
   return (d <= 64 && n_q > 128) ? 8 : 4;
 }
 
-template <int DT, int DH>
+template <int DT, int DH, bool CAUSAL>
 hipError_t launch_pairs(const SdpaArgs& a, hipStream_t st) {
   switch (pairs_waves(a.n_q, DH)) {
-    case 1: return launch_pairs_nw<DT, DH, 1>(a, st);
-    case 2: return launch_pairs_nw<DT, DH, 2>(a, st);
-    case 4: return launch_pairs_nw<DT, DH, 4>(a, st);
-    default: return launch_pairs_nw<DT, DH, (DH <= 64 ? 8 : 4)>(a, st);
+    case 1: return launch_pairs_nw<DT, DH, CAUSAL, 1>(a, st);
+    case 2: return launch_pairs_nw<DT, DH, CAUSAL, 2>(a, st);
+    case 4: return launch_pairs_nw<DT, DH, CAUSAL, 4>(a, st);
+    default: return launch_pairs_nw<DT, DH, CAUSAL, (DH <= 64 ? 8 : 4)>(a, st);
   }
 }
 
 template <int DT, int DH, bool CAUSAL>
 hipError_t launch_mfma(const SdpaArgs& a, hipStream_t st) {
   if constexpr (CAUSAL && SDPA_CAUSAL_PAIRS && DH >= 64) {
-    return launch_pairs<DT, DH>(a, st);
+    return launch_pairs<DT, DH, true>(a, st);
   } else {
     if (use_split(a.n_q, a.n_k, (int64_t)a.B * a.H, CAUSAL))
       return launch_split<DT, DH, split_waves(DH)>(a, st);
