@@ -453,7 +453,7 @@ def main():
                      "kernel": "sdpa_fwd_kernel<bf16, d 64, non-causal, 4 waves>"},
         "roofline_causal": {"bound": "mfma", "achieved": round(ach_c, 2), "peak": PEAK_BF16_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(ach_c / PEAK_BF16_TFLOPS, 4),
-                            "kernel": "sdpa_fwd_kernel<bf16, d 64, causal, 4 waves>"},
+                            "kernel": "sdpa_fwd_kernel<bf16, d 64, causal pair layout, 8 waves>"},
     }
     if not args.no_other_configs:
         res["other_configs"] = other_configs(dev, stream)
