@@ -166,13 +166,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   const int nqb = PAIRS ? (p.n_q + NW * 32 - 1) / (NW * 32)
                   : SPLIT ? (p.n_q + 31) / 32 : CAUSAL ? (units + NW - 1) / NW : (p.n_q + BM - 1) / BM;
   const uint32_t total = (uint32_t)nqb * p.B * p.H;
-  // pairs: consecutive workgroups are different heads at the same rows,
-  // highest rows (most work) first; they spread over the XCDs round-robin
-  // (grouping each head's workgroups on one XCD measured no faster)
+  // pairs: highest rows (most work) first.  Workgroup x runs on XCD x % 8;
+  // when the heads divide evenly, each XCD takes its own heads and walks
+  // them row group by row group from the top, so a head's K/V is read from
+  // memory by one XCD (round-robin heads measured as fast but re-read them:
+  // 79 MB against 67 MB per launch); otherwise consecutive workgroups are
+  // different heads at the same rows.
   const uint32_t t = PAIRS ? blockIdx.x : xcd_remap(blockIdx.x, total);
   const uint32_t nbh = (uint32_t)p.B * p.H;
-  const int bh = PAIRS ? (int)(t % nbh) : (int)(t / nqb);
-  const int qb = PAIRS ? nqb - 1 - (int)(t / nbh) : (int)(t % nqb);
+  const bool xcd_heads = PAIRS && nbh % 8 == 0;
+  const uint32_t hpx = nbh / 8, xk = t / 8;
+  const int bh = !PAIRS ? (int)(t / nqb)
+                 : xcd_heads ? (int)((t % 8) * hpx + xk % hpx) : (int)(t % nbh);
+  const int qb = !PAIRS ? (int)(t % nqb)
+                 : xcd_heads ? nqb - 1 - (int)(xk / hpx) : nqb - 1 - (int)(t / nbh);
   const int b = bh / p.H, hh = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is the same for all lanes of a wave: readfirstlane makes

@@ -89,10 +89,12 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json, commands):
         wb = w.get(name, 0.0) * 1024.0 * write_factor
         res["kernels"][name] = {"fetch_kib": f[name], "write_kib": w.get(name),
                                 "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
-    # the bench workload is the largest launch of each mode among the plain
-    # d = 64 kernels (template arguments: dtype, d, causal, waves, key split,
-    # window); smaller launches of other workloads may be in the same run
-    targs = re.compile(r"sdpa_fwd_kernel<(\d+), (\d+), (true|false), (\d+), (true|false), (true|false)>")
+    # the bench workload is the largest launch of each mode among the d = 64
+    # kernels without key split or window (template arguments: dtype, d,
+    # causal, waves, key split, window, pair layout); smaller launches of
+    # other workloads may be in the same run
+    targs = re.compile(r"sdpa_fwd_kernel<(\d+), (\d+), (true|false), (\d+), (true|false), "
+                       r"(true|false)(?:, (?:true|false))?>")
     for mode, causal in (("noncausal", "false"), ("causal", "true")):
         cands = []
         for k, v in res["kernels"].items():
