@@ -2,17 +2,19 @@
 // flash kernel template (instantiated by sdpa_fwd.hip and sdpa_window.hip).
 //
 // Computes, per (batch, head), O = softmax(scale · Q·Kᵀ) · V with the
-// causal mask (key c visible to query r iff c <= r) and/or a per-batch
-// valid key length -- eq. (1) of "Lire « Attention Is All You Need »"
-// (nickwang.xyz), §3.2.1, with the decoder mask of "Trois usages de
-// l'attention dans le modèle" (forbidden scores set to -inf before the
-// softmax).  The n_q × n_k score matrix is never formed: key/value tiles
+// causal mask (key c visible to query r iff c <= r), a restricted window
+// (r − left <= c <= r + right), and/or a per-batch valid key length -- eq.
+// (1) of "Lire « Attention Is All You Need »" (nickwang.xyz), §3.2.1, with
+// the decoder mask of "Trois usages de l'attention dans le modèle"
+// (forbidden scores set to -inf before the softmax) and the restricted
+// self-attention of §4.  The n_q × n_k score matrix is never formed: key/value tiles
 // stream through LDS and an online softmax (running max m and sum l per
 // query row, fp32) rescales the fp32 output accumulator.
 //
-// Work decomposition.  A workgroup is 4 waves (2 with the causal mask) of
-// one (batch, head); each wave owns 64 query rows as two blocks of 32.
-// 64-key K and V tiles pass through a 2-stage LDS ring.  Scores are formed
+// Work decomposition.  A workgroup is 1, 2 or 4 waves of one (batch,
+// head); each wave owns 64 query rows as two blocks of 32 (the forms below
+// -- causal, key split, pair layout, window -- change which rows and keys a
+// wave takes).  64-key K and V tiles pass through a 2-stage LDS ring.  Scores are formed
 // transposed, Sᵀ = K·Qᵀ, with the 32x32x16 MFMA: K is the A operand (rows
 // = keys, read from LDS), Q the B operand (columns = queries, kept in
 // registers for the whole kernel).  In the MFMA result layout every lane
@@ -40,21 +42,22 @@
 // is the same for every m.  A tile is first exponentiated against the
 // current m; as long as each lane's partial row sum stays ≤ 2^8 (so every
 // weight is ≤ 2^8) the tile is accepted as is.  Otherwise -- and on the
-// first tile of a wave -- the wave takes the exact path: row max, new m,
+// first tile of a block -- the wave takes the exact path: row max, new m,
 // rescale of O and l by exp2((m_old − m_new)·c), and the weights again.
 // The row sums add the fp32 weights (P·V uses them rounded to the input
 // dtype; the two differ by at most 2^-9 relative per weight).
 //
 // Loads.  K and V tiles go from memory straight into LDS (buffer loads with
-// an LDS destination), with 16-byte chunks of each 128-byte row permuted
-// (XOR with a few bits of the key) so that the fragment reads of a 16-lane
-// phase hit all 64 banks once.  The buffer range ends at the valid key
+// an LDS destination), with the 16-byte chunks of each row permuted (XOR
+// with a few bits of the key, per head dimension) so that the fragment
+// reads of a phase hit all 64 banks once.  The buffer range ends at the valid key
 // length, so rows past it read as 0 without per-lane branches: whatever
 // the memory there holds -- NaN included -- has no effect, matching the
-// reading that a masked key has weight exactly 0.  Causal tiles entirely
-// above the diagonal are never loaded, tiles a whole wave cannot see are
-// skipped by that wave, and only the diagonal and key-length boundary tiles
-// evaluate the per-element mask.
+// reading that a masked key has weight exactly 0; masked causal and window
+// tiles clear the V values of keys no row of the wave sees.  Causal tiles
+// entirely above the diagonal are never loaded, tiles a whole wave cannot
+// see are skipped by that wave, and only the diagonal, window-edge and
+// key-length boundary tiles evaluate the per-element mask.
 
 #pragma once
 
