@@ -250,9 +250,9 @@ def other_configs(dev, stream, iters=100):
 
 
 # Table 3 row (A) of the nickwang.xyz page: d_model fixed at 512, h and
-# d_k = d_v = d_model / h varied (the FLOPs stay the same); plus d_k 128 at
-# d_model 1024 (row (C)).
-HEAD_DIM_VARIANTS = ((8, 64), (32, 16), (16, 32), (4, 128), (8, 128))
+# d_k = d_v = d_model / h varied from 32 heads of 16 to one head of 512 (the
+# FLOPs stay the same); plus d_k 128 at d_model 1024 (row (C)).
+HEAD_DIM_VARIANTS = ((8, 64), (32, 16), (16, 32), (4, 128), (2, 256), (1, 512), (8, 128))
 
 
 def head_dim_sweep(dev, stream, B=4, n=4096, iters=50, settle_s=1.0):

@@ -78,11 +78,10 @@ enum {
  *   seq_lens[b] keys (key padding; clamped to [0, n_k]).  Masked K/V rows
  *   are never read, so their contents (NaN included) have no effect.
  * scale: any finite float; the pages use 1/sqrt(d_k).
- * Supported: BF16/F16 with d_k = d_v in {16, 32, 64, 128} and n_k·d_k·2
- *   bytes < 2 GiB (MFMA flash kernel); F32 with d_k = d_v in {16, 32, 64,
- *   128}.  The head-dimension variants are those of [N] Table 3 row (A)
- *   (d_model fixed, h and d_k = d_model / h varied); d_k = 512 (h = 1) is
- *   not supported.
+ * Supported: BF16/F16 with d_k = d_v in {16, 32, 64, 128, 256, 512} and
+ *   n_k·d_k·2 bytes < 2 GiB (MFMA kernels); F32 with d_k = d_v in {16, 32,
+ *   64, 128}.  The head-dimension variants are those of [N] Table 3 row (A)
+ *   (d_model fixed, h and d_k = d_model / h varied, down to h = 1).
  * O must not overlap Q, K, V or seq_lens (MHA_ERR_ALIAS).
  */
 int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype, int64_t B,
@@ -98,7 +97,7 @@ int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype
  * neighbourhood of size 2w + 1 is left = right = w; left >= n_q - 1 with
  * right = 0 is the causal mask; seq_lens masks keys as in mha_sdpa.  A row
  * whose window holds no valid key gives 0.  Only the key tiles inside some
- * row's window are read.  Supported: as mha_sdpa.
+ * row's window are read.  Supported: as mha_sdpa with d_k <= 128.
  */
 int mha_sdpa_window(const void* Q, const void* K, const void* V, void* O, int32_t dtype,
                     int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v,
@@ -121,7 +120,7 @@ int mha_sdpa_window(const void* Q, const void* K, const void* V, void* O, int32_
  *   Wo [h·d_k, d_model]               row blocks in the same head order
  *   out [B, n_q, d_model]             (written)
  * d_k = d_v = d_model / h.  Supported: BF16/F16 with d_k in {16, 32, 64,
- *   128} and d_model a multiple of 64.
+ *   128, 256, 512} and d_model a multiple of 64.
  * mask_kind: NONE (encoder self / cross) or CAUSAL (decoder self).
  * kv_lens: NULL or device int32[B], key padding as in mha_sdpa.
  * workspace: device memory of at least mha_forward_workspace_size() bytes,

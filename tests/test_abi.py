@@ -58,7 +58,8 @@ def _sdpa(dtype=M.MHA_BF16, B=1, h=1, n_q=8, n_k=8, d_k=64, d_v=64, scale=0.125,
     (dict(n_k=9, mask=M.MHA_MASK_CAUSAL), M.MHA_ERR_SHAPE),
     (dict(scale=float("nan")), M.MHA_ERR_INVALID_ARG),
     (dict(scale=float("inf")), M.MHA_ERR_INVALID_ARG),
-    (dict(d_k=256, d_v=256), M.MHA_ERR_UNSUPPORTED),
+    (dict(d_k=1024, d_v=1024), M.MHA_ERR_UNSUPPORTED),
+    (dict(d_k=256, d_v=256, dtype=M.MHA_F32), M.MHA_ERR_UNSUPPORTED),
     (dict(d_k=48, d_v=48), M.MHA_ERR_UNSUPPORTED),
     (dict(d_k=64, d_v=32), M.MHA_ERR_UNSUPPORTED),
     (dict(dtype=M.MHA_F32, d_k=48, d_v=48), M.MHA_ERR_UNSUPPORTED),
@@ -99,7 +100,7 @@ def _fwd(dtype=M.MHA_BF16, B=2, n_q=8, n_k=8, d_model=128, h=2, mask=M.MHA_MASK_
     (dict(dtype=5), M.MHA_ERR_DTYPE),
     (dict(dtype=M.MHA_F32), M.MHA_ERR_UNSUPPORTED),
     (dict(d_model=129, h=2), M.MHA_ERR_SHAPE),
-    (dict(d_model=512, h=2), M.MHA_ERR_UNSUPPORTED),     # head dim 256
+    (dict(d_model=2048, h=2), M.MHA_ERR_UNSUPPORTED),    # head dim 1024
     (dict(d_model=96, h=2), M.MHA_ERR_UNSUPPORTED),      # head dim 48
     (dict(d_model=96, h=3), M.MHA_ERR_UNSUPPORTED),      # head dim 32, d_model not a multiple of 64
     (dict(h=0), M.MHA_ERR_SHAPE),
@@ -202,9 +203,9 @@ def test_forward_add_norm_workspace_size():
     assert L.mha_forward_add_norm_workspace_size(B, n_q, n_k, dm, 0, M.MHA_BF16) == 0
 
 
-def _win(left=1, right=1, dtype=M.MHA_BF16, n_q=8, n_k=8, O=0x300000):
+def _win(left=1, right=1, dtype=M.MHA_BF16, n_q=8, n_k=8, O=0x300000, d=64):
     L = M.lib()
-    return L.mha_sdpa_window(0x1000, 0x100000, 0x200000, O, dtype, 1, 1, n_q, n_k, 64, 64, 0.125,
+    return L.mha_sdpa_window(0x1000, 0x100000, 0x200000, O, dtype, 1, 1, n_q, n_k, d, d, 0.125,
                              left, right, None, None)
 
 
@@ -213,6 +214,7 @@ def _win(left=1, right=1, dtype=M.MHA_BF16, n_q=8, n_k=8, O=0x300000):
     (dict(right=-5), M.MHA_ERR_INVALID_ARG),
     (dict(O=0x1000), M.MHA_ERR_ALIAS),
     (dict(dtype=4), M.MHA_ERR_DTYPE),
+    (dict(d=256), M.MHA_ERR_UNSUPPORTED),          # the window needs d <= 128
 ])
 def test_window_rejects(kw, code):
     assert _win(**kw) == code

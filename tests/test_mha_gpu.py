@@ -98,6 +98,8 @@ def test_ragged(case):
     (2, 150, 150, 512, 4, False, "none", [150, 9]),     # d_k = 128
     (2, 200, 200, 1024, 8, False, "causal", None),      # d_model 1024, d_k = 128
     (2, 64, 64, 256, 8, False, "none", None),           # d_model 256, d_k = 32
+    (2, 90, 90, 512, 1, False, "causal", None),         # h = 1, d_k = 512
+    (2, 40, 120, 512, 2, True, "none", [120, 17]),      # h = 2, d_k = 256
 ])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_head_dims(case, dtype):

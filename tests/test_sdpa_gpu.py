@@ -169,6 +169,33 @@ def test_head_dims(dtype, d, case):
     _check(got, exp, dtype, f"{dtype} d={d} {case}")
 
 
+# Wide heads (d_k = 256, 512: Table 3 row (A) of the nickwang.xyz page with
+# h = 2 and h = 1 at d_model 512): the kernel that splits d across the waves
+# of a workgroup; ragged query blocks and 32-key tiles, key padding, both
+# masks.
+WIDE_CASES = [
+    # (B, h, n_q, n_k, mask, lens)
+    (2, 1, 70, 70, "causal", None),
+    (3, 2, 50, 97, "none", [97, 31, 0]),
+    (1, 1, 257, 257, "causal", [200]),
+    (2, 1, 33, 600, "none", None),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [256, 512])
+@pytest.mark.parametrize("case", WIDE_CASES,
+                         ids=lambda c: "x".join(map(str, c[:4])) + f"_{c[4]}" + ("_lens" if c[5] else ""))
+def test_wide_heads(dtype, d, case):
+    B, h, n_q, n_k, mask, lens = case
+    scale = 1 / math.sqrt(d)
+    ins = synth.sdpa_inputs(900 + d + n_q, B, h, n_q, n_k, d, dtype=dtype)
+    note(f"sdpa {dtype} wide d={d} {case}")
+    got = _run(ins, dtype, mask, lens, scale=scale)
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], scale, MASKS[mask], lens)
+    _check(got, exp, dtype, f"{dtype} wide d={d} {case}")
+
+
 @pytest.mark.parametrize("d", [16, 32, 128])
 @pytest.mark.parametrize("mask", ["none", "causal"])
 def test_head_dims_four_wave(d, mask):

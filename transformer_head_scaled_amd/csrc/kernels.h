@@ -30,6 +30,8 @@ struct SdpaArgs {
 hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float scale, hipStream_t st);
 // the flash kernel's window form (bf16 / fp16), sdpa_window.hip
 hipError_t launch_sdpa_window(const SdpaArgs& a, int dtype, int d, hipStream_t st);
+// wide heads, d = 256 or 512 (bf16 / fp16, no window), sdpa_wide.hip
+hipError_t launch_sdpa_wide(const SdpaArgs& a, int dtype, int causal, int d, hipStream_t st);
 int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t n_k, int64_t heads);
 
 // One GEMM C = A·W of the projections: A [M, K] row-major (row stride lda),

@@ -144,8 +144,11 @@ static int sdpa_impl(const char* fn, const void* Q, const void* K, const void* V
   if (dtype == MHA_F32) {
     if (d_k != d_v || (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128))
       return fail(MHA_ERR_UNSUPPORTED, "%s: f32 needs d_k == d_v in {16,32,64,128}", fn);
-  } else if (d_k != d_v || (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128)) {
-    return fail(MHA_ERR_UNSUPPORTED, "%s: bf16/f16 needs d_k == d_v in {16,32,64,128}", fn);
+  } else if (d_k != d_v || (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128 && d_k != 256 &&
+                            d_k != 512)) {
+    return fail(MHA_ERR_UNSUPPORTED, "%s: bf16/f16 needs d_k == d_v in {16,32,64,128,256,512}", fn);
+  } else if (window && d_k > 128) {
+    return fail(MHA_ERR_UNSUPPORTED, "%s: the window needs d_k <= 128", fn);
   } else if (n_k * d_k * 2 > kMaxBufferBytes) {
     return fail(MHA_ERR_UNSUPPORTED, "%s: one head's K/V exceeds 2 GiB (n_k %lld)", fn,
                 (long long)n_k);
@@ -259,8 +262,8 @@ static int forward_impl(const char* fn, const void* x_q, const void* x_kv, const
     return fail(MHA_ERR_SHAPE, "%s: causal mask needs n_q == n_k", fn);
   if (dtype == MHA_F32) return fail(MHA_ERR_UNSUPPORTED, "%s: f32 is not implemented", fn);
   const int64_t d = d_model / h;
-  if (d != 16 && d != 32 && d != 64 && d != 128)
-    return fail(MHA_ERR_UNSUPPORTED, "%s: head dim %lld (needs 16, 32, 64 or 128)", fn,
+  if (d != 16 && d != 32 && d != 64 && d != 128 && d != 256 && d != 512)
+    return fail(MHA_ERR_UNSUPPORTED, "%s: head dim %lld (needs 16, 32, 64, 128, 256 or 512)", fn,
                 (long long)d);
   if (d_model % 64 != 0)  // the projection GEMMs tile N and K by 64
     return fail(MHA_ERR_UNSUPPORTED, "%s: d_model %lld is not a multiple of 64", fn,

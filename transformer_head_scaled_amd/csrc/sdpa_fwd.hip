@@ -224,6 +224,7 @@ hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float sc
       default: return hipErrorInvalidValue;
     }
   }
+  if (d > 128) return launch_sdpa_wide(a, dtype, causal, d, st);
   if (a.window) return launch_sdpa_window(a, dtype, d, st);
   return dtype == DT_BF16 ? launch_dim<DT_BF16>(a, causal, d, st) : launch_dim<DT_F16>(a, causal, d, st);
 }

@@ -1,0 +1,273 @@
+// Scaled dot-product attention for wide heads, d = 256 and 512 (bf16 /
+// fp16): eq. (1) of "Lire « Attention Is All You Need »" (nickwang.xyz),
+// §3.2.1, for the head sizes of its Table 3 row (A) with few heads
+// (d_model 512 with h = 1 gives d_k = d_v = 512).
+//
+// One 32-row query block per workgroup of 4 waves, the head dimension split
+// across the waves: wave w owns columns [w·D/4, (w+1)·D/4) of Q, K, V and O.
+// The output accumulator of a block at d = 512 would need 256 registers
+// per lane in one wave; split four ways it needs 64.  The scores need the
+// whole contraction over d, so per 32-key tile each wave forms the partial
+// Sᵀ over its columns (MFMA, as in the d <= 128 kernel: Sᵀ = K·Qᵀ, one
+// query row per lane), the four partials are added through LDS (each wave
+// adds them in the same order, so all four hold the same scores), every
+// wave runs the same softmax step on them, and each wave accumulates its own
+// columns of Oᵀ = Vᵀ·Pᵀ.  K and V tiles of 32 keys go straight from memory
+// into a 2-stage LDS ring (buffer loads with an LDS destination, one 1 KB
+// row piece per instruction at d = 512); their 16-byte chunks are permuted
+// by key bits as in the d = 128 layout, so the fragment reads spread over
+// all banks.  Causal tiles past the block's diagonal are not computed and
+// rows past the key length read as zero.  The softmax keeps a running max:
+// the exact form, each tile's row max first (the scores are in registers,
+// so there is no recomputation to save).
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mha {
+
+namespace {
+
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
+  constexpr int NW = 4, BN = 32, NSTAGE = 2;
+  constexpr int DS = D / NW;         // columns per wave
+  constexpr int NST = DS / 16;       // 16-deep MFMA steps of a partial score block
+  constexpr int NDB = DS / 32;       // 32-row blocks of this wave's Oᵀ
+  constexpr int CR = D / 8;          // 16-byte chunks per K/V row
+  constexpr int RPP = 64 / CR;       // rows per 1 KB load piece (< 1 at d = 512: a row is 1 or 2 KB)
+  constexpr int PPR = CR / 64;       // 1 KB pieces per row (d = 512: 1; d = 256: 0 -> 2 rows per piece)
+  static_assert(D == 256 || D == 512, "wide head dimension");
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NSTAGE][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NSTAGE][BN * D];
+  __shared__ __attribute__((aligned(16))) float Sx[NW][16 * 64];  // partial scores, lane-contiguous
+
+  const int nqb = (p.n_q + 31) / 32;
+  const uint32_t nbh = (uint32_t)p.B * p.H;
+  // causal: the highest blocks (most keys) first
+  const int qb = CAUSAL ? nqb - 1 - (int)(blockIdx.x / nbh) : (int)(blockIdx.x / nbh);
+  const int bh = (int)(blockIdx.x % nbh);
+  const int b = bh / p.H, hh = bh % p.H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int row0 = qb * 32;
+
+  int n_eff = p.n_k;
+  if (p.lens) n_eff = min(max(p.lens[b], 0), p.n_k);
+  int kend = n_eff;
+  if (CAUSAL) kend = min(kend, row0 + 32);
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  const uint16_t* Qg = (const uint16_t*)p.Q + b * p.q_sb + hh * p.q_sh;
+  const uint16_t* Kg = (const uint16_t*)p.K + b * p.k_sb + hh * p.k_sh;
+  const uint16_t* Vg = (const uint16_t*)p.V + b * p.v_sb + hh * p.v_sh;
+  uint16_t* Og = (uint16_t*)p.O + b * p.o_sb + hh * p.o_sh;
+  const uint64_t kaddr = (uint64_t)(uintptr_t)Kg;
+  const u32x4 krs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)kaddr),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(kaddr >> 32) & 0xffffu),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((int64_t)n_eff * p.k_sr * 2)),
+                     0x00020000u};
+  const uint64_t vaddr = (uint64_t)(uintptr_t)Vg;
+  const u32x4 vrs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)vaddr),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(vaddr >> 32) & 0xffffu),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((int64_t)n_eff * p.v_sr * 2)),
+                     0x00020000u};
+
+  // this wave's Q columns (B operand), resident
+  u32x4 qf[NST];
+  {
+    const int row = row0 + l32;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row < p.n_q) v = *(const u32x4*)(Qg + (int64_t)row * p.q_sr + wave * DS + st * 16 + hi * 8);
+      qf[st] = p.neg ? flip_signs(v) : v;
+    }
+  }
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+  const float c = p.c;
+
+  // ---- staging: a tile is BN rows of D/8 16-byte chunks, chunk c of key k
+  // stored at c ^ (k & 15) (K; the 16 keys of a fragment read phase then
+  // cover the 16 bank groups of a 256-byte segment) and c ^ 4·(k & 3) (V;
+  // a transposing read phase of 4 keys covers the four quarters).  Each
+  // wave instruction fills 1 KB: lane i writes chunk position i of a row
+  // (d = 512) or of one of two rows (d = 256).
+  constexpr int PIECES = BN * D * 2 / 1024;  // 1 KB pieces per tile
+  constexpr int CPW = PIECES / NW;
+  auto piece_src = [&](int r, bool is_v) __attribute__((always_inline)) {
+    const int key = (PPR >= 1) ? r : 2 * r + lane / CR;  // PPR >= 1: one row per piece
+    const int pos = lane % CR;
+    const int ch = is_v ? (pos ^ (4 * (key & 3))) : (pos ^ (key & 15));
+    return (uint32_t)(((int64_t)key * (is_v ? p.v_sr : p.k_sr) + ch * 8) * 2);
+  };
+  auto gload = [&](int tile, int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int r = wave * CPW + i;
+      load_lds_b128(krs,
+                    __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+                        __attribute__((address_space(3))) void*)&Ks[stage][r * 512]),
+                    piece_src(r, false) + (uint32_t)(tile * BN * p.k_sr * 2));
+      load_lds_b128(vrs,
+                    __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+                        __attribute__((address_space(3))) void*)&Vs[stage][r * 512]),
+                    piece_src(r, true) + (uint32_t)(tile * BN * p.v_sr * 2));
+    }
+  };
+  // K fragment st of this wave: key l32, chunk (wave·DS)/8 + 2·st + hi
+  auto kfrag = [&](int buf, int st) __attribute__((always_inline)) {
+    const int ch = (wave * DS) / 8 + 2 * st + hi;
+    return *(const u32x4*)&Ks[buf][l32 * D + ((ch ^ (l32 & 15)) * 8)];
+  };
+  // Vᵀ fragment (t2, db): d = wave·DS + db·32 + l32, keys of the 16-key step
+  // t2 in the score-register order, two transposing reads of 4 keys
+  const int i16 = lane & 15;
+  const int v_key_l = 4 * hi + (i16 >> 2);
+  const int v_col = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+  auto vfrag = [&](int buf, int t2, int db) __attribute__((always_inline)) {
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int key = t2 * 16 + 8 * e + v_key_l;
+      const int d = wave * DS + db * 32 + v_col;
+      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)&Vs[buf][key * D + (((d >> 3) ^ (4 * (key & 3))) * 8) + (d & 7)]);
+      const u32x2 w = __builtin_bit_cast(u32x2, v);
+      r[2 * e] = w[0];
+      r[2 * e + 1] = w[1];
+    }
+    return r;
+  };
+
+  if (ntiles > 0) gload(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j % NSTAGE;
+    if (j + 1 < ntiles) gload(j + 1, (j + 1) % NSTAGE);
+    // partial Sᵀ over this wave's columns, to LDS
+    f32x16 sp = {};
+#pragma unroll
+    for (int st = 0; st < NST; ++st) sp = mfma_32x32x16<DT>(kfrag(buf, st), qf[st], sp);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Sx[wave][i * 64 + lane] = sp[i];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    // the full scores: the four partials, added in wave order
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      s[i] = ((Sx[0][i * 64 + lane] + Sx[1][i * 64 + lane]) + Sx[2][i * 64 + lane]) +
+             Sx[3][i * 64 + lane];
+    // mask: key offset in the tile of register i is 8·(i / 4) + 4·hi + i % 4
+    const int row = row0 + l32;
+    const int lim = (CAUSAL ? min(n_eff, row + 1) : n_eff) - j * BN - 4 * hi;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int off = 8 * (i >> 2) + (i & 3);
+      if (off >= lim) s[i] = -INFINITY;
+    }
+    // online softmax, exact: the tile's row max first
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = pair_max(mx);
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
+    const float mc = (m_new == -INFINITY ? 0.f : m_new) * c;
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    uint32_t pw[8];
+    float rs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i], c, -mc));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i + 1], c, -mc));
+      pw[i] = pack2<DT>(e0, e1);
+      rs += e0 + e1;
+    }
+    l += rs;
+    // this wave's columns of Oᵀ += Vᵀ·Pᵀ (keys whose weight is 0 but whose
+    // value row lies past the causal diagonal of every row: cleared)
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const u32x4 bv = {pw[4 * t2], pw[4 * t2 + 1], pw[4 * t2 + 2], pw[4 * t2 + 3]};
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        u32x4 vf = vfrag(buf, t2, db);
+        if (CAUSAL) {
+          // keys past the block's last row are seen by no row of the block
+          const int k0 = j * BN + t2 * 16 + 4 * hi;
+          const int vhi = min(n_eff, min(row0 + 31, p.n_q - 1) + 1);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int ka = k0 + ((2 * w) & 3) + 8 * ((2 * w) >> 2);
+            const uint32_t keep = (ka < vhi ? 0x0000ffffu : 0u) | (ka + 1 < vhi ? 0xffff0000u : 0u);
+            vf[w] &= keep;
+          }
+        }
+        o[db] = mfma_32x32x16<DT>(vf, bv, o[db]);
+      }
+    }
+    // the next tile has landed, every wave is past its reads of this stage
+    // and of the exchange area
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("s_barrier" ::: "memory");
+  }
+
+  // normalise and store this wave's columns of the lane's row
+  const float L = pair_sum(l);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int row = row0 + l32;
+  if (row < p.n_q) {
+    uint16_t* orow = Og + (int64_t)row * p.o_sr + wave * DS;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + g * 8 + hi * 4;
+        const u32x2 w = {pack2<DT>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                         pack2<DT>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+        *(u32x2*)(orow + d) = w;
+      }
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_d(const SdpaArgs& a, int causal, hipStream_t st) {
+  const int64_t grid = (a.n_q + 31) / 32 * (int64_t)a.B * a.H;
+  if (causal)
+    hipLaunchKernelGGL((sdpa_wide_kernel<DT, D, true>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((sdpa_wide_kernel<DT, D, false>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sdpa_wide(const SdpaArgs& a, int dtype, int causal, int d, hipStream_t st) {
+  if (a.window) return hipErrorInvalidValue;  // not offered for wide heads
+  if (dtype == DT_BF16) {
+    if (d == 256) return launch_d<DT_BF16, 256>(a, causal, st);
+    if (d == 512) return launch_d<DT_BF16, 512>(a, causal, st);
+  } else if (dtype == DT_F16) {
+    if (d == 256) return launch_d<DT_F16, 256>(a, causal, st);
+    if (d == 512) return launch_d<DT_F16, 512>(a, causal, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mha
