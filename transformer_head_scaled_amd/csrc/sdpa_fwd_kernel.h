@@ -751,24 +751,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
     asm volatile("s_barrier" ::: "memory");
   };
 
-  // One step of the key loop: start the loads of tile j + NSTAGE - 1,
-  // compute tile j (both blocks, block 1 only, or nothing), barrier.
-  // WHAT: 0 = nothing, 1 = block 1 only, 2 = both blocks.
+  // One step of the key loop: start the loads of tile j + NSTAGE - 1 (K and
+  // V both at the top: V issued mid-tile, as the pair layout does, measured
+  // 1.5-2.5 % slower here), compute tile j (both blocks, block 1 only, or
+  // nothing), barrier.  WHAT: 0 = nothing, 1 = block 1 only, 2 = both blocks.
   auto step = [&](int j, auto masked, auto what) __attribute__((always_inline)) {
     constexpr int WHAT = decltype(what)::value;
     const int buf = j % NSTAGE;
     const bool more = j + NSTAGE - 1 < ntiles;
-    if (more) gload_k(j + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE);
-    auto load_v = [&]() __attribute__((always_inline)) {
-      if (more) gload_v(j + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE);
-    };
+    if (more) {
+      gload_k(j + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE);
+      gload_v(j + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE);
+    }
+    auto nothing = []() __attribute__((always_inline)) {};
     const int kbase = j * BN;
     if constexpr (WHAT == 2)
-      tile(masked, buf, kbase, load_v);
+      tile(masked, buf, kbase, nothing);
     else if constexpr (WHAT == 1)
-      tile_hi(masked, buf, kbase, load_v);
-    else
-      load_v();
+      tile_hi(masked, buf, kbase, nothing);
     // Before the barrier, this wave's loads of tile j + 1 have landed: only
     // the four issued in this step may still be outstanding (none if it
     // issued none, or with two stages, where tile j + 1 is this step's).
