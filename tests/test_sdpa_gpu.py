@@ -106,6 +106,21 @@ def test_four_wave_workgroups_ragged_lens(dtype):
         _check(got[b, i], exp, dtype, f"{dtype} 4-wave head ({b},{i}) len {lens[b]}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_short_heads(dtype, d):
+    """[64,32,50,70] unmasked with key lengths: 2048 heads of fewer than 64
+    query rows, enough waves for the one-wave two-block workgroups (fewer
+    heads take the pair layout).  Every head is compared."""
+    lens = [70, 69, 64, 63, 1, 0, 33, 100] * 8
+    scale = 1 / math.sqrt(d)
+    ins = synth.sdpa_inputs(77 + d, 64, 32, 50, 70, d, dtype=dtype)
+    note(f"sdpa {dtype} d={d} [64,32,50,70] key lengths")
+    got = _run(ins, dtype, "none", lens, scale=scale)
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], scale, oracle.MASK_NONE, lens)
+    _check(got, exp, dtype, f"{dtype} d={d} 2048 short heads")
+
+
 # ragged shapes: tails of the 128-row query blocks and 64-key tiles, tiny
 # sizes, cross-attention n_q != n_k, key padding including 0 and > n_k
 RAGGED = [

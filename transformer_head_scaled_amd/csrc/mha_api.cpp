@@ -202,7 +202,7 @@ static int sdpa_impl(const char* fn, const void* Q, const void* K, const void* V
                  fn, (int)dtype, (long long)B, (long long)h, (long long)n_q, (long long)n_k,
                  (long long)d_k, (int)mask_kind, window ? a.win_left : -1, window ? a.win_right : -1,
                  seq_lens ? "yes" : "no",
-                 mha::sdpa_rows_per_workgroup(dtype, mask_kind == MHA_MASK_CAUSAL, n_q, n_k, B * h), 4.0 * d_k * vis * B * h,
+                 mha::sdpa_rows_per_workgroup(dtype, mask_kind == MHA_MASK_CAUSAL, n_q, n_k, B * h, (int)d_k), 4.0 * d_k * vis * B * h,
                  (double)es * B * h * (2 * n_q * d_k + 2 * n_k * d_k));
   }
   const hipError_t e = mha::launch_sdpa(a, dtype, mask_kind == MHA_MASK_CAUSAL, (int)d_k, scale,

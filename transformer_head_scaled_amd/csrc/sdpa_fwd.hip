@@ -167,13 +167,28 @@ hipError_t launch_pairs(const SdpaArgs& a, hipStream_t st) {
   }
 }
 
+// Unmasked, d >= 64: the pair layout (32 query rows a wave) when the
+// two-block layout (64 a wave) would leave fewer than two waves on each
+// SIMD: twice the waves, and one workgroup of eight then fills a compute
+// unit.  0 selects two blocks for all.
+#ifndef SDPA_NONCAUSAL_PAIRS
+#define SDPA_NONCAUSAL_PAIRS 1
+#endif
+constexpr int64_t kSimds = 256 * 4;  // 256 compute units of 4 SIMDs
+bool noncausal_pairs(int64_t n_q, int64_t heads, int d) {
+  const int64_t waves2 = heads * ((n_q + 63) / 64);  // waves of the two-block layout
+  return SDPA_NONCAUSAL_PAIRS && d >= 64 && waves2 < 2 * kSimds;
+}
+
 template <int DT, int DH, bool CAUSAL>
 hipError_t launch_mfma(const SdpaArgs& a, hipStream_t st) {
+  const int64_t heads = (int64_t)a.B * a.H;
   if constexpr (CAUSAL && SDPA_CAUSAL_PAIRS && DH >= 64) {
     return launch_pairs<DT, DH, true>(a, st);
   } else {
-    if (use_split(a.n_q, a.n_k, (int64_t)a.B * a.H, CAUSAL))
+    if (use_split(a.n_q, a.n_k, heads, CAUSAL))
       return launch_split<DT, DH, split_waves(DH)>(a, st);
+    if (!CAUSAL && noncausal_pairs(a.n_q, heads, DH)) return launch_pairs<DT, DH, false>(a, st);
     switch (waves_per_wg(a.n_q, (int64_t)a.B * a.H, CAUSAL)) {
       case 1: return launch_nw<DT, DH, CAUSAL, 1>(a, st);
       case 2: return launch_nw<DT, DH, CAUSAL, 2>(a, st);
@@ -207,10 +222,12 @@ hipError_t launch_f32(const SdpaArgs& a, float scale, int causal, hipStream_t st
 
 }  // namespace
 
-int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t n_k, int64_t heads) {
+int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t n_k, int64_t heads, int d) {
   if (dtype == DT_F32) return 64;
-  if (causal && SDPA_CAUSAL_PAIRS) return pairs_waves(n_q, 64) * 32;  // (d >= 64)
+  if (d > 128) return 32;  // the wide-head kernel
+  if (causal && SDPA_CAUSAL_PAIRS && d >= 64) return pairs_waves(n_q, d) * 32;
   if (use_split(n_q, n_k, heads, causal != 0)) return 32;
+  if (!causal && noncausal_pairs(n_q, heads, d)) return pairs_waves(n_q, d) * 32;
   return waves_per_wg(n_q, heads, causal != 0) * 64;
 }
 

@@ -311,9 +311,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   constexpr int LPW = SPLIT ? PIECES : CPW;  // pieces this wave loads per tile
   const int kvw = SPLIT ? wave : 0;          // this wave's LDS ring
 
-  // issue this wave's two LDS-destination loads of K (or V) for one tile.
-  // The K and V halves are issued at different points of a step, so that
-  // the waves of a compute unit do not all queue their loads at once.
+  // issue this wave's LDS-destination loads of K (or V) for one tile
   auto gload_k = [&](int tile, int stage) __attribute__((always_inline)) {
     if (!loader) return;
 #pragma unroll
