@@ -17,9 +17,13 @@
 // row piece per instruction at d = 512); their 16-byte chunks are permuted
 // by key bits as in the d = 128 layout, so the fragment reads spread over
 // all banks.  Causal tiles past the block's diagonal are not computed and
-// rows past the key length read as zero.  The softmax keeps a running max:
-// the exact form, each tile's row max first (the scores are in registers,
-// so there is no recomputation to save).
+// rows past the key length read as zero; only the tiles that hold a masked
+// key for some row of the block evaluate the per-element mask.  The softmax
+// has no per-tile max, as in the d <= 128 kernel: a tile's weights are
+// formed against the row's current reference value and accepted while each
+// lane's partial row sum stays <= 2^8; otherwise (and on the first tile)
+// the tile's row max sets a new reference and O and l are rescaled.  The
+// four waves hold the same scores, so they take the same path.
 
 #include <type_traits>
 
@@ -43,7 +47,11 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NSTAGE][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NSTAGE][BN * D];
-  __shared__ __attribute__((aligned(16))) float Sx[NW][16 * 64];  // partial scores, lane-contiguous
+  // partial scores: lane l's 16 values as four 16-byte chunks, chunk c
+  // stored at c ^ ((l >> 2) & 3) (the 16 lanes of a 16-byte access phase
+  // then cover all 64 banks)
+  __shared__ __attribute__((aligned(16))) float Sx[NW][64 * 16];
+  constexpr float kAccept = 256.f;
 
   const int nqb = (p.n_q + 31) / 32;
   const uint32_t nbh = (uint32_t)p.B * p.H;
@@ -91,8 +99,13 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f, mc = 0.f;
   const float c = p.c;
+  // first key masked for some row of the block (the block's first row sees
+  // keys up to itself) and first key no row of the block sees (causal)
+  const int mask_from = CAUSAL ? min(n_eff, row0 + 1) : n_eff;
+  const int vhi = min(n_eff, min(row0 + 31, p.n_q - 1) + 1);
+  const int sx_sw = (lane >> 2) & 3;
 
   // ---- staging: a tile is BN rows of D/8 16-byte chunks, chunk c of key k
   // stored at c ^ (k & 15) (K; the 16 keys of a fragment read phase then
@@ -159,45 +172,61 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
 #pragma unroll
     for (int st = 0; st < NST; ++st) sp = mfma_32x32x16<DT>(kfrag(buf, st), qf[st], sp);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Sx[wave][i * 64 + lane] = sp[i];
+    for (int q = 0; q < 4; ++q)
+      *(f32x4*)&Sx[wave][lane * 16 + 4 * (q ^ sx_sw)] = f32x4{sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]};
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
     // the full scores: the four partials, added in wave order
     f32x16 s;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      s[i] = ((Sx[0][i * 64 + lane] + Sx[1][i * 64 + lane]) + Sx[2][i * 64 + lane]) +
-             Sx[3][i * 64 + lane];
-    // mask: key offset in the tile of register i is 8·(i / 4) + 4·hi + i % 4
-    const int row = row0 + l32;
-    const int lim = (CAUSAL ? min(n_eff, row + 1) : n_eff) - j * BN - 4 * hi;
+    for (int q = 0; q < 4; ++q) {
+      const int at = lane * 16 + 4 * (q ^ sx_sw);
+      const f32x4 v = ((*(const f32x4*)&Sx[0][at] + *(const f32x4*)&Sx[1][at]) + *(const f32x4*)&Sx[2][at]) +
+                      *(const f32x4*)&Sx[3][at];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int off = 8 * (i >> 2) + (i & 3);
-      if (off >= lim) s[i] = -INFINITY;
+      for (int e = 0; e < 4; ++e) s[4 * q + e] = v[e];
     }
-    // online softmax, exact: the tile's row max first
-    float mx = -INFINITY;
+    if (j * BN + BN > mask_from) {
+      // mask: key offset in the tile of register i is 8·(i / 4) + 4·hi + i % 4
+      const int row = row0 + l32;
+      const int lim = (CAUSAL ? min(n_eff, row + 1) : n_eff) - j * BN - 4 * hi;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m, mx);
-    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
-    const float mc = (m_new == -INFINITY ? 0.f : m_new) * c;
-    m = m_new;
-    l *= alpha;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      for (int i = 0; i < 16; ++i) {
+        const int off = 8 * (i >> 2) + (i & 3);
+        if (off >= lim) s[i] = -INFINITY;
+      }
+    }
     uint32_t pw[8];
-    float rs = 0.f;
+    auto weights = [&]() __attribute__((always_inline)) {
+      float r0 = 0.f, r1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i], c, -mc));
-      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i + 1], c, -mc));
-      pw[i] = pack2<DT>(e0, e1);
-      rs += e0 + e1;
+      for (int i = 0; i < 8; ++i) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i], c, -mc));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i + 1], c, -mc));
+        pw[i] = pack2<DT>(e0, e1);
+        r0 += e0;
+        r1 += e1;
+      }
+      return r0 + r1;
+    };
+    float rs = weights();
+    // `!(rs <= kAccept)` is also true for NaN
+    const bool reject = (m == -INFINITY) || !(rs <= kAccept);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(reject) != 0, 0)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m, mx);
+      const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
+      mc = (m_new == -INFINITY ? 0.f : m_new) * c;
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      rs = weights();
     }
     l += rs;
     // this wave's columns of Oᵀ += Vᵀ·Pᵀ (keys whose weight is 0 but whose
@@ -208,10 +237,9 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         u32x4 vf = vfrag(buf, t2, db);
-        if (CAUSAL) {
+        if (CAUSAL && j * BN + BN > vhi) {
           // keys past the block's last row are seen by no row of the block
           const int k0 = j * BN + t2 * 16 + 4 * hi;
-          const int vhi = min(n_eff, min(row0 + 31, p.n_q - 1) + 1);
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const int ka = k0 + ((2 * w) & 3) + 8 * ((2 * w) >> 2);
