@@ -13,8 +13,9 @@
 // adds them in the same order, so all four hold the same scores), every
 // wave runs the same softmax step on them, and each wave accumulates its own
 // columns of Oᵀ = Vᵀ·Pᵀ.  K and V tiles of 32 keys go straight from memory
-// into a 2-stage LDS ring (buffer loads with an LDS destination, one 1 KB
-// row piece per instruction at d = 512); their 16-byte chunks are permuted
+// into one LDS buffer each (buffer loads with an LDS destination, one 1 KB
+// row piece per instruction at d = 512), K and V loads staggered so that
+// each lands while the other half of the tile is computed; their 16-byte chunks are permuted
 // by key bits as in the d = 128 layout, so the fragment reads spread over
 // all banks.  Causal tiles past the block's diagonal are not computed and
 // rows past the key length read as zero; only the tiles that hold a masked
@@ -36,7 +37,7 @@ namespace {
 
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
-  constexpr int NW = 4, BN = 32, NSTAGE = 2;
+  constexpr int NW = 4, BN = 32;
   constexpr int DS = D / NW;         // columns per wave
   constexpr int NST = DS / 16;       // 16-deep MFMA steps of a partial score block
   constexpr int NDB = DS / 32;       // 32-row blocks of this wave's Oᵀ
@@ -45,8 +46,10 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
   constexpr int PPR = CR / 64;       // 1 KB pieces per row (d = 512: 1; d = 256: 0 -> 2 rows per piece)
   static_assert(D == 256 || D == 512, "wide head dimension");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[NSTAGE][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[NSTAGE][BN * D];
+  // one K and one V tile: 80 KB in all at d = 512 (48 KB at d = 256), so
+  // that two (three) workgroups share a compute unit
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * D];
   // partial scores: lane l's 16 values as four 16-byte chunks, chunk c
   // stored at c ^ ((l >> 2) & 3) (the 16 lanes of a 16-byte access phase
   // then cover all 64 banks)
@@ -121,38 +124,44 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
     const int ch = is_v ? (pos ^ (4 * (key & 3))) : (pos ^ (key & 15));
     return (uint32_t)(((int64_t)key * (is_v ? p.v_sr : p.k_sr) + ch * 8) * 2);
   };
-  auto gload = [&](int tile, int stage) __attribute__((always_inline)) {
+  auto gload_k = [&](int tile) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int r = wave * CPW + i;
       load_lds_b128(krs,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-                        __attribute__((address_space(3))) void*)&Ks[stage][r * 512]),
+                        __attribute__((address_space(3))) void*)&Ks[r * 512]),
                     piece_src(r, false) + (uint32_t)(tile * BN * p.k_sr * 2));
+    }
+  };
+  auto gload_v = [&](int tile) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int r = wave * CPW + i;
       load_lds_b128(vrs,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-                        __attribute__((address_space(3))) void*)&Vs[stage][r * 512]),
+                        __attribute__((address_space(3))) void*)&Vs[r * 512]),
                     piece_src(r, true) + (uint32_t)(tile * BN * p.v_sr * 2));
     }
   };
   // K fragment st of this wave: key l32, chunk (wave·DS)/8 + 2·st + hi
-  auto kfrag = [&](int buf, int st) __attribute__((always_inline)) {
+  auto kfrag = [&](int st) __attribute__((always_inline)) {
     const int ch = (wave * DS) / 8 + 2 * st + hi;
-    return *(const u32x4*)&Ks[buf][l32 * D + ((ch ^ (l32 & 15)) * 8)];
+    return *(const u32x4*)&Ks[l32 * D + ((ch ^ (l32 & 15)) * 8)];
   };
   // Vᵀ fragment (t2, db): d = wave·DS + db·32 + l32, keys of the 16-key step
   // t2 in the score-register order, two transposing reads of 4 keys
   const int i16 = lane & 15;
   const int v_key_l = 4 * hi + (i16 >> 2);
   const int v_col = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
-  auto vfrag = [&](int buf, int t2, int db) __attribute__((always_inline)) {
+  auto vfrag = [&](int t2, int db) __attribute__((always_inline)) {
     u32x4 r;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int key = t2 * 16 + 8 * e + v_key_l;
       const int d = wave * DS + db * 32 + v_col;
       const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)&Vs[buf][key * D + (((d >> 3) ^ (4 * (key & 3))) * 8) + (d & 7)]);
+          (lds_s16x4*)&Vs[key * D + (((d >> 3) ^ (4 * (key & 3))) * 8) + (d & 7)]);
       const u32x2 w = __builtin_bit_cast(u32x2, v);
       r[2 * e] = w[0];
       r[2 * e + 1] = w[1];
@@ -160,32 +169,34 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
     return r;
   };
 
-  if (ntiles > 0) gload(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-  asm volatile("s_barrier" ::: "memory");
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j % NSTAGE;
-    if (j + 1 < ntiles) gload(j + 1, (j + 1) % NSTAGE);
-    // partial Sᵀ over this wave's columns, to LDS
+  // partial Sᵀ over this wave's columns for the keys in LDS
+  auto spart = [&]() __attribute__((always_inline)) {
     f32x16 sp = {};
 #pragma unroll
-    for (int st = 0; st < NST; ++st) sp = mfma_32x32x16<DT>(kfrag(buf, st), qf[st], sp);
+    for (int st = 0; st < NST; ++st) sp = mfma_32x32x16<DT>(kfrag(st), qf[st], sp);
+    return sp;
+  };
+  auto put_sx = [&](const f32x16& sp) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *(f32x4*)&Sx[wave][lane * 16 + 4 * (q ^ sx_sw)] = f32x4{sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]};
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
-    // the full scores: the four partials, added in wave order
+      *(f32x4*)&Sx[wave][lane * 16 + 4 * (q ^ sx_sw)] =
+          f32x4{sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]};
+  };
+  // the full scores: the four partials, added in wave order
+  auto get_sx = [&]() __attribute__((always_inline)) {
     f32x16 s;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int at = lane * 16 + 4 * (q ^ sx_sw);
-      const f32x4 v = ((*(const f32x4*)&Sx[0][at] + *(const f32x4*)&Sx[1][at]) + *(const f32x4*)&Sx[2][at]) +
-                      *(const f32x4*)&Sx[3][at];
+      const f32x4 v = ((*(const f32x4*)&Sx[0][at] + *(const f32x4*)&Sx[1][at]) +
+                       *(const f32x4*)&Sx[2][at]) + *(const f32x4*)&Sx[3][at];
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[4 * q + e] = v[e];
     }
+    return s;
+  };
+  // mask, weights and softmax state of tile j; P (packed) into pw
+  auto softmax = [&](f32x16& s, int j, uint32_t (&pw)[8]) __attribute__((always_inline)) {
     if (j * BN + BN > mask_from) {
       // mask: key offset in the tile of register i is 8·(i / 4) + 4·hi + i % 4
       const int row = row0 + l32;
@@ -196,7 +207,6 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
         if (off >= lim) s[i] = -INFINITY;
       }
     }
-    uint32_t pw[8];
     auto weights = [&]() __attribute__((always_inline)) {
       float r0 = 0.f, r1 = 0.f;
 #pragma unroll
@@ -229,14 +239,17 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
       rs = weights();
     }
     l += rs;
-    // this wave's columns of Oᵀ += Vᵀ·Pᵀ (keys whose weight is 0 but whose
-    // value row lies past the causal diagonal of every row: cleared)
+  };
+  // this wave's columns of Oᵀ += Vᵀ·Pᵀ for the values in LDS (keys whose
+  // weight is 0 but whose value row lies past the causal diagonal of every
+  // row: cleared)
+  auto pv = [&](int j, const uint32_t (&pw)[8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const u32x4 bv = {pw[4 * t2], pw[4 * t2 + 1], pw[4 * t2 + 2], pw[4 * t2 + 3]};
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        u32x4 vf = vfrag(buf, t2, db);
+        u32x4 vf = vfrag(t2, db);
         if (CAUSAL && j * BN + BN > vhi) {
           // keys past the block's last row are seen by no row of the block
           const int k0 = j * BN + t2 * 16 + 4 * hi;
@@ -250,10 +263,35 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
         o[db] = mfma_32x32x16<DT>(vf, bv, o[db]);
       }
     }
-    // the next tile has landed, every wave is past its reads of this stage
-    // and of the exchange area
-    __builtin_amdgcn_s_waitcnt(0x0070);
+  };
+
+  // One K and one V buffer: K of tile j + 1 is loaded once every wave has
+  // formed its partials of tile j (it lands during the softmax and P·V), V
+  // of tile j + 1 once every wave is past P·V of tile j (it lands during
+  // the partials and the exchange).  The other workgroups of the compute
+  // unit fill the waits.  (Two stages of K and V, with or without forming
+  // the next tile's partials during the softmax, measured 4-43 % slower:
+  // they leave room for one workgroup less.)
+  if (ntiles > 0) {
+    gload_k(0);
+    gload_v(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+  for (int j = 0; j < ntiles; ++j) {
+    put_sx(spart());
+    // exchange writes visible, V(j) landed, every wave past its K reads
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
+    if (j + 1 < ntiles) gload_k(j + 1);
+    f32x16 s = get_sx();
+    uint32_t pw[8];
+    softmax(s, j, pw);
+    pv(j, pw);
+    // K(j + 1) landed, every wave past its V and exchange reads
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    if (j + 1 < ntiles) gload_v(j + 1);
   }
 
   // normalise and store this wave's columns of the lane's row
