@@ -416,6 +416,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 
   // fragment holds key 4·hi + (j & 3) + 8·(j >> 2) of its 16-key step; dword
   // w holds elements 2w (low half) and 2w + 1.
   auto zero_unseen_v = [&](u32x4 (&vf)[2][2][NDB], int kbase) __attribute__((always_inline)) {
+    if (kbase >= vlo && kbase + BN <= vhi) return;  // (wave-uniform) every key of the tile seen
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll

@@ -23,9 +23,22 @@ hipError_t launch_win_nw(const SdpaArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Waves per workgroup: as for the plain kernel, but at most two while the
+// window spans fewer than 2048 keys besides the row itself.  A workgroup
+// loads the key tiles of all its rows' windows and every wave takes part in
+// every step, so a wave idles through the tiles only its neighbours see,
+// with nothing to cover the next tile's load; 128 rows a workgroup halve
+// that.  Measured on [4,8,4096,64], reach w on both sides, four waves
+// against two: w 0 36.7 / 25.3 µs, 64 41.2 / 31.6, 256 55.4 / 41.8, 1024
+// 97.9 / 88.9, 2048 141.8 / 145.3 (one wave: slower from w 64 on).
+int window_waves(const SdpaArgs& a) {
+  const int w = waves_per_wg(a.n_q, (int64_t)a.B * a.H, false);
+  return (w > 2 && (int64_t)a.win_left + a.win_right < 2048) ? 2 : w;
+}
+
 template <int DT, int DH>
 hipError_t launch_win(const SdpaArgs& a, hipStream_t st) {
-  switch (waves_per_wg(a.n_q, (int64_t)a.B * a.H, false)) {
+  switch (window_waves(a)) {
     case 1: return launch_win_nw<DT, DH, 1>(a, st);
     case 2: return launch_win_nw<DT, DH, 2>(a, st);
     default: return launch_win_nw<DT, DH, 4>(a, st);
