@@ -93,7 +93,9 @@ def test_window_head_dims(d):
 
 @pytest.mark.parametrize("left,right", [(128, 128), (300, 0), (0, 0), (2000, 2000)])
 def test_window_four_wave(left, right):
-    """[8,16,1000,1000] bf16: four-wave workgroups; one whole head per batch."""
+    """[8,16,1000,1000] bf16: enough row blocks for four-wave workgroups,
+    which windows under 2048 keys run as two-wave ones ((2000, 2000) covers
+    every key and runs the unmasked kernel); one whole head per batch."""
     lens = [1000, 999, 500, 64, 63, 1, 0, 1100]
     ins = synth.sdpa_inputs(870 + left, 8, 16, 1000, 1000, 64, dtype="bf16")
     note(f"window bf16 [8,16,1000,1000] ({left},{right})")
@@ -101,6 +103,23 @@ def test_window_four_wave(left, right):
     Q, K, V = (ins[n][1] for n in "QKV")
     for b in range(8):
         i = (5 * b + 3) % 16
+        exp = oracle.sdpa(Q[b:b + 1, i:i + 1], K[b:b + 1, i:i + 1], V[b:b + 1, i:i + 1], 0.125,
+                          oracle.MASK_NONE, [lens[b]], window=(left, right))[0, 0]
+        _check(got[b, i], exp, "bf16", f"window ({left},{right}) head ({b},{i}) len {lens[b]}")
+
+
+def test_window_wide_four_wave():
+    """[8,16,2600,2600] bf16, window (1500, 600): 2101 keys, wide enough for
+    four-wave workgroups, covering neither side; key lengths as above; one
+    whole head per batch."""
+    left, right = 1500, 600
+    lens = [2600, 2599, 1500, 64, 63, 1, 0, 3000]
+    ins = synth.sdpa_inputs(611, 8, 16, 2600, 2600, 64, dtype="bf16")
+    note(f"window bf16 [8,16,2600,2600] ({left},{right})")
+    got = _run(ins, "bf16", left, right, lens)
+    Q, K, V = (ins[n][1] for n in "QKV")
+    for b in range(8):
+        i = (7 * b + 3) % 16
         exp = oracle.sdpa(Q[b:b + 1, i:i + 1], K[b:b + 1, i:i + 1], V[b:b + 1, i:i + 1], 0.125,
                           oracle.MASK_NONE, [lens[b]], window=(left, right))[0, 0]
         _check(got[b, i], exp, "bf16", f"window ({left},{right}) head ({b},{i}) len {lens[b]}")
