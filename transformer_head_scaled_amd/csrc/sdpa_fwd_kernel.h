@@ -129,11 +129,17 @@ constexpr int split_waves(int d) {
 // which take the places of the two blocks of the default layout in the tile
 // code (S of one tile computed while the other's exponentials run).
 // Workgroups are launched longest first (the work of a block grows with its
-// rows).  Without the mask it runs too, but measured slower than the
-// default layout (d 64: 873 against 948 TFLOP/s), so it is not launched so.
+// rows).  Without the mask it runs too; at full occupancy it measured slower
+// than the default layout (d 64: 873 against 948 TFLOP/s), so unmasked
+// heads take it only where 64 rows a wave would leave SIMDs without a
+// second wave (sdpa_fwd.hip).
 template <int DT, int DH, bool CAUSAL, int NW, bool SPLIT = false, bool WINDOW = false,
           bool PAIRS = false>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 1 || DH > 64 || SPLIT) ? 1 : 2, 2))) void sdpa_fwd_kernel(SdpaArgs p) {
+// (Two waves per SIMD as the register target, except where one is all there
+// can be: one-wave workgroups, d = 128, the key split, and two-wave pair
+// workgroups, whose 64 KB of LDS leaves room for two per compute unit.)
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
+    (NW == 1 || DH > 64 || SPLIT || (PAIRS && NW <= 2)) ? 1 : 2, 2))) void sdpa_fwd_kernel(SdpaArgs p) {
   static_assert(!(SPLIT && CAUSAL), "the key split is for the unmasked case");
   static_assert(!(WINDOW && (CAUSAL || SPLIT)), "the window has its own mask");
   static_assert(!PAIRS || (!SPLIT && !WINDOW), "the pair layout has no key split or window");

@@ -42,7 +42,6 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
   constexpr int NST = DS / 16;       // 16-deep MFMA steps of a partial score block
   constexpr int NDB = DS / 32;       // 32-row blocks of this wave's Oᵀ
   constexpr int CR = D / 8;          // 16-byte chunks per K/V row
-  constexpr int RPP = 64 / CR;       // rows per 1 KB load piece (< 1 at d = 512: a row is 1 or 2 KB)
   constexpr int PPR = CR / 64;       // 1 KB pieces per row (d = 512: 1; d = 256: 0 -> 2 rows per piece)
   static_assert(D == 256 || D == 512, "wide head dimension");
 
