@@ -239,7 +239,7 @@ def other_configs(dev, stream, iters=100):
     med, mn = time_calls(call6, stream, iters)
     cmed, _ = time_calls(call6, stream, max(iters // 4, 10), flush)
     nbytes = w["h"] * int(lens.sum()) * w["d"] * 2 * 2 + 2 * w["B"] * w["h"] * w["n_q"] * w["d"] * 2
-    res[w["name"]] = {"call": "mha_sdpa (key split)", "us_median": round(med, 2), "us_min": round(mn, 2),
+    res[w["name"]] = {"call": "mha_sdpa (one-row decoding kernel)", "us_median": round(med, 2), "us_min": round(mn, 2),
                       "us_median_cold": round(cmed, 2),
                       "gbs": round(nbytes / (med * 1e-6) / 1e9, 1),
                       "gbs_cold": round(nbytes / (cmed * 1e-6) / 1e9, 1),

@@ -80,6 +80,8 @@ def test_workload_big_cross(dtype):
     (1, 1, 1, 64, 1, False, "none", None),              # h = 1, d_model = 64
     (4, 130, 70, 128, 2, True, "none", None),
     (3, 450, 450, 1024, 16, False, "none", [450, 200, 1]),  # 128 x 128 GEMM tiles, ragged rows
+    (4, 1, 777, 512, 8, True, "none", [777, 600, 1, 0]),     # one decoder position: the decoding-step kernel
+    (2, 1, 600, 1024, 8, True, "none", None),               # the same at d_k = 128
 ])
 def test_ragged(case):
     B, n_q, n_k, dm, h, cross, mask, lens = case

@@ -287,6 +287,35 @@ def test_decode_key_split(dtype, d, case):
     _check(got, exp, dtype, f"{dtype} decode d={d} {case}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_padding_nan_inf(dtype, d):
+    """One query row against 777 cached keys (the decoding-step kernel) with
+    key lengths 777, 700, 513, 8, 0: the K and V rows past each length hold
+    NaN and +/-inf, which must have no effect (a masked key's weight is
+    exactly 0 and its value never enters).  Lengths that are not a multiple
+    of a wave's run leave its last step partly past the length."""
+    B, h, n_k = 5, 3, 777
+    lens = [777, 700, 513, 8, 0]
+    ins = synth.sdpa_inputs(450 + d, B, h, 1, n_k, d, dtype=dtype)
+    bad = {"bf16": (0x7fc0, 0x7f80, 0xff80), "f16": (0x7e00, 0x7c00, 0xfc00)}[dtype]
+    for name in "KV":
+        st = ins[name][0].view(np.uint16)
+        for b, n in enumerate(lens):
+            st[b, :, n:, 0::3] = bad[0]
+            st[b, :, n:, 1::3] = bad[1]
+            st[b, :, n:, 2::3] = bad[2]
+    scale = 1 / math.sqrt(d)
+    note(f"sdpa {dtype} decode d={d} NaN/inf past the key lengths")
+    got = _run(ins, dtype, "none", lens, scale=scale)
+    Q, K, V = (ins[n][1] for n in "QKV")
+    exp = np.zeros_like(got)
+    for b, n in enumerate(lens):   # the oracle sees the valid keys only
+        if n:
+            exp[b] = oracle.sdpa(Q[b:b + 1], K[b:b + 1, :, :n], V[b:b + 1, :, :n], scale)[0]
+    _check(got, exp, dtype, f"{dtype} decode d={d} with NaN/inf padding")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 1.0])
 def test_unusual_scales(dtype, scale):

@@ -18,8 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libmha.so")
-SOURCES = ["mha_api.cpp", "sdpa_fwd.hip", "sdpa_window.hip", "sdpa_wide.hip", "gemm_proj.hip",
-           "add_norm.hip"]
+SOURCES = ["mha_api.cpp", "sdpa_fwd.hip", "sdpa_window.hip", "sdpa_wide.hip", "sdpa_decode.hip",
+           "gemm_proj.hip", "add_norm.hip"]
 ARCH = "gfx950"
 
 

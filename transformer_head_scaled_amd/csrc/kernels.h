@@ -32,6 +32,10 @@ hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float sc
 hipError_t launch_sdpa_window(const SdpaArgs& a, int dtype, int d, hipStream_t st);
 // wide heads, d = 256 or 512 (bf16 / fp16, no window), sdpa_wide.hip
 hipError_t launch_sdpa_wide(const SdpaArgs& a, int dtype, int causal, int d, hipStream_t st);
+// one query row against a long key/value cache (bf16 / fp16, d = 64, 128,
+// no mask but key lengths), sdpa_decode.hip
+bool sdpa_decode_applies(const SdpaArgs& a, int dtype, int causal, int d);
+hipError_t launch_sdpa_decode(const SdpaArgs& a, int dtype, int d, hipStream_t st);
 int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t n_k, int64_t heads, int d);
 
 // One GEMM C = A·W of the projections: A [M, K] row-major (row stride lda),

@@ -231,6 +231,7 @@ hipError_t launch_f32(const SdpaArgs& a, float scale, int causal, hipStream_t st
 int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t n_k, int64_t heads, int d) {
   if (dtype == DT_F32) return 64;
   if (d > 128) return 32;  // the wide-head kernel
+  if (!causal && n_q == 1 && (d == 64 || d == 128) && n_k >= 512) return 1;  // the decoding-step kernel
   if (causal && SDPA_CAUSAL_PAIRS && d >= 64) return pairs_waves(n_q, d, true) * 32;
   if (use_split(n_q, n_k, heads, causal != 0)) return 32;
   if (!causal && noncausal_pairs(n_q, heads, d)) return pairs_waves(n_q, d, false) * 32;
@@ -249,6 +250,7 @@ hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float sc
   }
   if (d > 128) return launch_sdpa_wide(a, dtype, causal, d, st);
   if (a.window) return launch_sdpa_window(a, dtype, d, st);
+  if (sdpa_decode_applies(a, dtype, causal, d)) return launch_sdpa_decode(a, dtype, d, st);
   return dtype == DT_BF16 ? launch_dim<DT_BF16>(a, causal, d, st) : launch_dim<DT_F16>(a, causal, d, st);
 }
 
