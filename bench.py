@@ -450,7 +450,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(ach_nc, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach_nc / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "sdpa_fwd_kernel<bf16, d 64, non-causal, 4 waves>"},
+                     "kernel": "sdpa_fwd_kernel<bf16, d 64, non-causal, 8 waves>"},
         "roofline_causal": {"bound": "mfma", "achieved": round(ach_c, 2), "peak": PEAK_BF16_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(ach_c / PEAK_BF16_TFLOPS, 4),
                             "kernel": "sdpa_fwd_kernel<bf16, d 64, causal pair layout, 8 waves>"},

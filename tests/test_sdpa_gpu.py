@@ -107,6 +107,24 @@ def test_four_wave_workgroups_ragged_lens(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_eight_wave_workgroups_ragged_lens(dtype):
+    """[8,16,2100,2100] unmasked with key lengths (0, 1, 63, 64, 1000, 2099,
+    2100, and one past n_k): 2048 query rows or more take 8-wave (512-row)
+    workgroups, here with a ragged last one and key-length boundary tiles.
+    One whole head per batch is compared."""
+    lens = [2100, 2099, 1000, 64, 63, 1, 0, 3000]
+    ins = synth.sdpa_inputs(37, 8, 16, 2100, 2100, 64, dtype=dtype)
+    note(f"sdpa {dtype} [8,16,2100,2100] key lengths {lens}")
+    got = _run(ins, dtype, "none", lens)
+    Q, K, V = (ins[n][1] for n in "QKV")
+    for b in range(8):
+        i = (3 * b + 2) % 16
+        exp = oracle.sdpa(Q[b:b + 1, i:i + 1], K[b:b + 1, i:i + 1], V[b:b + 1, i:i + 1], 0.125,
+                          oracle.MASK_NONE, [lens[b]])[0, 0]
+        _check(got[b, i], exp, dtype, f"{dtype} 8-wave head ({b},{i}) len {lens[b]}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_many_short_heads(dtype, d):
     """[64,32,50,70] unmasked with key lengths: 2048 heads of fewer than 64
