@@ -191,7 +191,9 @@ bool noncausal_pairs(int64_t n_q, int64_t heads, int d) {
 // into LDS then serves twice the rows.  Measured against 4 waves
 // (interleaved runs, identical results): [4,8,4096,64] +3.0 %,
 // [2,8,8192,64] +3.6 %, [8,8,2048,64] +2.2 %, [8,8,4096,64] +0.4 %.
-// (d = 128 holds one wave per SIMD, so 8 waves do not fit a compute unit.)
+// (d = 128 holds one wave per SIMD, so 8 waves do not fit a compute unit;
+// at d = 16 and 32, bound by the exponentials, 8 waves measured 5-8 %
+// slower.)
 bool noncausal_eight_waves(int64_t n_q, int64_t heads, int d) {
   return d == 64 && n_q >= 2048 && waves_per_wg(n_q, heads, false) == 4;
 }
@@ -204,8 +206,10 @@ hipError_t launch_mfma(const SdpaArgs& a, hipStream_t st) {
   } else {
     if (use_split(a.n_q, a.n_k, heads, CAUSAL))
       return launch_split<DT, DH, split_waves(DH)>(a, st);
-    if (!CAUSAL && noncausal_pairs(a.n_q, heads, DH)) return launch_pairs<DT, DH, false>(a, st);
-    if (!CAUSAL && noncausal_eight_waves(a.n_q, heads, DH)) return launch_nw<DT, DH, false, 8>(a, st);
+    if constexpr (!CAUSAL && DH >= 64)
+      if (noncausal_pairs(a.n_q, heads, DH)) return launch_pairs<DT, DH, false>(a, st);
+    if constexpr (!CAUSAL && DH == 64)
+      if (noncausal_eight_waves(a.n_q, heads, DH)) return launch_nw<DT, DH, false, 8>(a, st);
     switch (waves_per_wg(a.n_q, (int64_t)a.B * a.H, CAUSAL)) {
       case 1: return launch_nw<DT, DH, CAUSAL, 1>(a, st);
       case 2: return launch_nw<DT, DH, CAUSAL, 2>(a, st);
