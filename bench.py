@@ -32,7 +32,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sdpa_fwd_traffic.json")
 # the sources the attention kernel is compiled from (the traffic record is
 # tied to their hash)
 KERNEL_SRCS = [os.path.join(ROOT, "transformer_head_scaled_amd", "csrc", f)
-               for f in ("sdpa_fwd_kernel.h", "sdpa_fwd.hip", "device_common.h")]
+               for f in ("sdpa_fwd_kernel.h", "sdpa_fwd.hip", "device_common.h")] + [
+    os.path.join(ROOT, "transformer_head_scaled_amd", "build.py")]  # (its compiler flags)
 
 
 def sdpa_flops(B, h, n_q, n_k, d, causal):

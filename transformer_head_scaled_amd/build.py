@@ -20,6 +20,15 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libmha.so")
 SOURCES = ["mha_api.cpp", "sdpa_fwd.hip", "sdpa_window.hip", "sdpa_wide.hip", "sdpa_decode.hip",
            "gemm_proj.hip", "add_norm.hip"]
+# Per-source flags.  The flash attention kernel is scheduled with LLVM's
+# "max-memory-clause" strategy: the same instructions and results, measured
+# (interleaved runs) 1-2 % faster causal at d 64 and 128 and 2 % unmasked at
+# d 128, unchanged unmasked at d 64; the default, "max-ilp" and
+# "iterative-ilp" strategies measured no better.
+SOURCE_FLAGS = {
+    "sdpa_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+    "sdpa_window.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+}
 ARCH = "gfx950"
 
 
@@ -62,7 +71,7 @@ def build(verbose=False, extra=None):
     os.makedirs(LIBDIR, exist_ok=True)
     objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        futs = [ex.submit(_compile, s, o, extra) for s, o in zip(SOURCES, objs)]
+        futs = [ex.submit(_compile, s, o, SOURCE_FLAGS.get(s, []) + extra) for s, o in zip(SOURCES, objs)]
         for s, f in zip(SOURCES, futs):
             msg = f.result()
             if verbose and msg.strip():

@@ -23,7 +23,8 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SRCS = [os.path.join(ROOT, "transformer_head_scaled_amd", "csrc", f)
-               for f in ("sdpa_fwd_kernel.h", "sdpa_fwd.hip", "device_common.h")]
+               for f in ("sdpa_fwd_kernel.h", "sdpa_fwd.hip", "device_common.h")] + [
+    os.path.join(ROOT, "transformer_head_scaled_amd", "build.py")]  # (its compiler flags)
 COPY_BYTES = 512 << 20
 
 
