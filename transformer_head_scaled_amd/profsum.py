@@ -4,8 +4,11 @@
     python -m transformer_head_scaled_amd.profsum traffic <fetch_dir> <write_dir> \
         <copy_fetch_dir> <copy_write_dir> <out.json> "<commands>"
 
+    python -m transformer_head_scaled_amd.profsum counters <pmc_dir> <out.md> "<command>"
+
 ``stats`` turns a ``--kernel-trace --stats`` kernel_stats.csv into a markdown
-table.  ``traffic`` reads four ``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE,
+table.  ``counters`` turns one ``--pmc`` run of the SQ/GRBM counters below
+into per-kernel utilisation figures.  ``traffic`` reads four ``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE,
 for the attention bench and for a plain device copy of known size), scales
 each counter by known-bytes / counter-reading of the copy, and records the
 HBM bytes per attention launch together with a hash of the kernel source the
@@ -71,6 +74,71 @@ def counter_means(run_dir, counter):
     return {k: sum(v) / len(v) for k, v in agg.items()}
 
 
+SIMDS = 256 * 4  # MI355X: 256 compute units of 4 SIMDs
+CUS = 256
+XCDS = 8  # rocprofv3 reports GRBM_GUI_ACTIVE summed over the 8 XCDs
+COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+            "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES"]
+
+
+def counters_md(run_dir, out_md, command, top=10):
+    """Per kernel (mean over its dispatches): the MFMA busy fraction
+    (sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE times
+    the SIMD count, rocprofv3's MfmaUtil), the clock (GRBM_GUI_ACTIVE over
+    the dispatch time), VALU instructions per MFMA instruction, LDS bank
+    conflict cycles per LDS instruction and resident waves per CU, for the
+    kernels with the longest dispatches
+    (SQ_WAVE_CYCLES counts in units of 4 cycles).  GRBM_GUI_ACTIVE comes
+    summed over the XCDs: one XCD's count is the device's busy cycles."""
+    path = None
+    for dp, _, files in os.walk(run_dir):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                path = os.path.join(dp, fn)
+    if path is None:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    durs = collections.defaultdict(dict)
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            k = r["Kernel_Name"]
+            vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            durs[k][r["Dispatch_Id"]] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    rows = []
+    for k, cs in vals.items():
+        if "mha::" not in k:  # the library's kernels only
+            continue
+        m = {c: sum(v) / len(v) for c, v in cs.items()}
+        ns = sum(durs[k].values()) / len(durs[k])
+        g = m.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+        if g <= 0:
+            continue
+        rows.append((ns, k, len(durs[k]), ns / 1e3, g / ns,
+                     100.0 * m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (g * SIMDS),
+                     (m.get("SQ_INSTS_VALU", 0.0) / m["SQ_INSTS_MFMA"]) if m.get("SQ_INSTS_MFMA") else None,
+                     m.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(m.get("SQ_INSTS_LDS", 0.0), 1.0),
+                     4.0 * m.get("SQ_WAVE_CYCLES", 0.0) / (g * CUS)))
+    rows.sort(reverse=True)
+    lines = ["# rocprofv3 counters per kernel", "", "Command:", "", "```", command, "```", "",
+             "G = GRBM_GUI_ACTIVE / 8 (rocprofv3 sums it over the 8 XCDs): the device's busy "
+             "cycles. MFMA busy % = 100 · Σ SQ_VALU_MFMA_BUSY_CYCLES / (G · 1024 SIMDs), "
+             "rocprofv3's MfmaUtil; clock = G / dispatch time; waves/CU = 4 · SQ_WAVE_CYCLES / "
+             "(G · 256); SQ_INSTS_VALU counts the MFMAs too. Dispatch times are under counter "
+             "collection (kernels serialised): take durations from the kernel-trace summary; the "
+             "clock column means something only for dispatches much longer than that overhead "
+             "(the attention kernels of the first rows), and the shorter ones read above the "
+             "2.4 GHz maximum.", "",
+             "| kernel | dispatches | µs (under counters) | clock GHz | MFMA busy % | VALU insts / MFMA inst "
+             "| LDS bank-conflict cycles / LDS inst | waves / CU |",
+             "|---|---|---|---|---|---|---|---|"]
+    for _, k, n, us, ghz, busy, vpm, conf, wpc in rows[:top]:
+        vs = "n/a" if vpm is None else f"{vpm:.1f}"
+        lines.append(f"| `{k}` | {n} | {us:.1f} | {ghz:.2f} | {busy:.1f} | {vs} | {conf:.3f} | {wpc:.1f} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return rows
+
+
 def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json, commands):
     f = counter_means(fetch_dir, "FETCH_SIZE")
     w = counter_means(write_dir, "WRITE_SIZE")
@@ -114,6 +182,8 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json, commands):
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats_md(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "counters":
+        counters_md(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "traffic":
         print(json.dumps(traffic(*sys.argv[2:7], sys.argv[7]), indent=1))
     else:
