@@ -150,22 +150,31 @@ hipError_t launch_pairs_nw(const SdpaArgs& a, hipStream_t st) {
 
 // Waves per pair workgroup: eight (each loaded tile then serves 256 query
 // rows, as in the other layouts), four for d = 128 (one wave per SIMD),
-// short sequences and causal ones up to 2048 rows, fewer below 64 rows.
+// short sequences, causal ones up to 2048 rows and long ones with too few
+// heads for two eight-wave workgroups per CU, fewer below 64 rows.
 // Causal, d = 64, four against eight (interleaved runs): [16,8,512,64]
 // +13 %, [64,8,512,64] +18 %, [16,8,1024,64] +10 %, [8,8,2048,64] +4 %;
 // [4,8,4096,64] −3.5 %, [2,8,8192,64] −4.5 %.  Smaller workgroups balance
 // better where a head has few row blocks: the waves of one workgroup wait
 // for its longest row block at every barrier.
-int pairs_waves(int64_t n_q, int d, bool causal) {
+int pairs_waves(int64_t n_q, int64_t heads, int d, bool causal) {
   if (n_q <= 32) return 1;
   if (n_q <= 64) return 2;
   if (d > 64 || n_q <= 128 || (causal && n_q <= 2048)) return 4;
+  // Eight waves (one workgroup a CU) only while there are enough of those
+  // workgroups: with few heads they leave CUs idle.  Unmasked, at least one
+  // per CU ([1,8,2048,64]: 64 workgroups, four waves 332 against 247
+  // TFLOP/s; at 256 workgroups eight waves stay 5 % ahead); causal, at
+  // least two per CU, since its workgroups carry unequal work and the
+  // longest-first order needs a second round to even it out ([1,8,4096,64]:
+  // 128 workgroups, 362 against 267; [2,8,4096,64]: 256, 660 against 530).
+  if (n_q >= 2048 && (n_q + 255) / 256 * heads < (causal ? 2 : 1) * 256) return 4;
   return 8;
 }
 
 template <int DT, int DH, bool CAUSAL>
 hipError_t launch_pairs(const SdpaArgs& a, hipStream_t st) {
-  switch (pairs_waves(a.n_q, DH, CAUSAL)) {
+  switch (pairs_waves(a.n_q, (int64_t)a.B * a.H, DH, CAUSAL)) {
     case 1: return launch_pairs_nw<DT, DH, CAUSAL, 1>(a, st);
     case 2: return launch_pairs_nw<DT, DH, CAUSAL, 2>(a, st);
     case 4: return launch_pairs_nw<DT, DH, CAUSAL, 4>(a, st);
@@ -247,9 +256,9 @@ int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t n_k, int
   if (dtype == DT_F32) return 64;
   if (d > 128) return 32;  // the wide-head kernel
   if (!causal && n_q == 1 && (d == 64 || d == 128) && n_k >= 512) return 1;  // the decoding-step kernel
-  if (causal && SDPA_CAUSAL_PAIRS && d >= 64) return pairs_waves(n_q, d, true) * 32;
+  if (causal && SDPA_CAUSAL_PAIRS && d >= 64) return pairs_waves(n_q, heads, d, true) * 32;
   if (use_split(n_q, n_k, heads, causal != 0)) return 32;
-  if (!causal && noncausal_pairs(n_q, heads, d)) return pairs_waves(n_q, d, false) * 32;
+  if (!causal && noncausal_pairs(n_q, heads, d)) return pairs_waves(n_q, heads, d, false) * 32;
   if (!causal && noncausal_eight_waves(n_q, heads, d)) return 512;
   return waves_per_wg(n_q, heads, causal != 0) * 64;
 }
