@@ -164,11 +164,12 @@ int pairs_waves(int64_t n_q, int64_t heads, int d, bool causal) {
   // Eight waves (one workgroup a CU) only while there are enough of those
   // workgroups: with few heads they leave CUs idle.  Unmasked, at least one
   // per CU ([1,8,2048,64]: 64 workgroups, four waves 332 against 247
-  // TFLOP/s; at 256 workgroups eight waves stay 5 % ahead); causal, at
-  // least two per CU, since its workgroups carry unequal work and the
-  // longest-first order needs a second round to even it out ([1,8,4096,64]:
-  // 128 workgroups, 362 against 267; [2,8,4096,64]: 256, 660 against 530).
-  if (n_q >= 2048 && (n_q + 255) / 256 * heads < (causal ? 2 : 1) * 256) return 4;
+  // TFLOP/s; [4,8,1024,64]: 529 against 409; at 256 workgroups eight waves
+  // stay ahead); causal, at least two per CU, since its workgroups carry
+  // unequal work and the longest-first order needs a second round to even
+  // it out ([1,8,4096,64]: 128 workgroups, 362 against 267; [2,8,4096,64]:
+  // 256, 660 against 530).  (Fewer than four waves measured slower.)
+  if ((n_q + 255) / 256 * heads < (causal ? 2 : 1) * 256) return 4;
   return 8;
 }
 
