@@ -162,15 +162,25 @@ int pairs_waves(int64_t n_q, int64_t heads, int d, bool causal) {
   if (n_q <= 64) return 2;
   if (d > 64 || n_q <= 128 || (causal && n_q <= 2048)) return 4;
   // Eight waves (one workgroup a CU) only while there are enough of those
-  // workgroups: with few heads they leave CUs idle.  Unmasked, at least one
-  // per CU ([1,8,2048,64]: 64 workgroups, four waves 332 against 247
-  // TFLOP/s; [4,8,1024,64]: 529 against 409; at 256 workgroups eight waves
-  // stay ahead); causal, at least two per CU, since its workgroups carry
-  // unequal work and the longest-first order needs a second round to even
-  // it out ([1,8,4096,64]: 128 workgroups, 362 against 267; [2,8,4096,64]:
-  // 256, 660 against 530).  (Fewer than four waves measured slower.)
-  if ((n_q + 255) / 256 * heads < (causal ? 2 : 1) * 256) return 4;
-  return 8;
+  // workgroups.  Causal needs at least two per CU, since its workgroups
+  // carry unequal work and the longest-first order needs a second round to
+  // even it out ([1,8,4096,64]: 128 workgroups, four waves 362 against 267
+  // TFLOP/s; [2,8,4096,64]: 256, 660 against 530).  Unmasked, by the
+  // makespan below ([1,8,2048,64] 332 against 247, [4,8,1024,64] 529
+  // against 409, [16,8,640,64] 525 against 453, [24,8,640,64] 608 against
+  // 435; [2,8,4096,64] and [8,16,384,64] stay with eight).  (Fewer than four
+  // waves measured slower.)
+  if (causal) return (n_q + 255) / 256 * heads < 2 * 256 ? 4 : 8;
+  // Unmasked: the shorter estimated makespan, in rounds of 256 CUs.  An
+  // eight-wave workgroup fills a CU (two waves a SIMD), so a partial last
+  // round costs a whole one; four-wave workgroups pair up two a CU, and a
+  // last round of at most one a CU runs one wave a SIMD, measured ≈ 0.6 of a
+  // round.  Ties go to eight waves (each staged tile serves twice the rows).
+  const int64_t wg8 = (n_q + 255) / 256 * heads, wg4 = (n_q + 127) / 128 * heads;
+  const int64_t t8 = (wg8 + 255) / 256 * 10;
+  const int64_t rem4 = wg4 % 512;
+  const int64_t t4 = wg4 / 512 * 10 + (rem4 == 0 ? 0 : rem4 > 256 ? 10 : 6);
+  return t4 < t8 ? 4 : 8;
 }
 
 template <int DT, int DH, bool CAUSAL>
