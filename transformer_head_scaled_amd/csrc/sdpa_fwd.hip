@@ -214,8 +214,18 @@ bool noncausal_pairs(int64_t n_q, int64_t heads, int d) {
 // (d = 128 holds one wave per SIMD, so 8 waves do not fit a compute unit;
 // at d = 16 and 32, bound by the exponentials, 8 waves measured 5-8 %
 // slower.)
+// Only where eight-wave workgroups (one a CU) do not leave a ragged last
+// round: the same makespan estimate as for the pair layout, in rounds of
+// 256 CUs, ties to eight ([8,8,2560,64]: 320 eight-wave workgroups, four
+// waves 835 against 667 TFLOP/s; [12,8,2048,64] 939 against 773;
+// [4,8,4608,64] 796 against 634; balanced grids unchanged).
 bool noncausal_eight_waves(int64_t n_q, int64_t heads, int d) {
-  return d == 64 && n_q >= 2048 && waves_per_wg(n_q, heads, false) == 4;
+  if (!(d == 64 && n_q >= 2048 && waves_per_wg(n_q, heads, false) == 4)) return false;
+  const int64_t wg8 = (n_q + 511) / 512 * heads, wg4 = (n_q + 255) / 256 * heads;
+  const int64_t t8 = (wg8 + 255) / 256 * 10;
+  const int64_t rem4 = wg4 % 512;
+  const int64_t t4 = wg4 / 512 * 10 + (rem4 == 0 ? 0 : rem4 > 256 ? 10 : 6);
+  return t8 <= t4;
 }
 
 template <int DT, int DH, bool CAUSAL>
