@@ -88,6 +88,35 @@ def test_workload_long_b4_n4096_sampled(mask):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("shape,mask", [
+    ((1, 3, 2304, 64), "causal"),   # few heads: four-wave pair workgroups past 2048 rows
+    ((1, 4, 1536, 64), "none"),     # unmasked pair layout, four waves by the makespan rule
+    ((8, 8, 2560, 64), "none"),     # two-block layout, four waves (ragged eight-wave round)
+])
+def test_workgroup_size_rules_sampled(shape, mask):
+    """Shapes whose workgroup size comes from the grid-size rules (few heads,
+    ragged last rounds): one whole head, plus sampled rows of every head."""
+    B, H, n, d = shape
+    ins = synth.sdpa_inputs(57, B, H, n, n, d, dtype="bf16")
+    note(f"sdpa bf16 {mask} {list(shape)}")
+    got = _run(ins, "bf16", mask)
+    Q, K, V = (ins[x][1] for x in "QKV")
+    mk = MASKS[mask]
+    exp, _ = oracle.attention_head(Q[B - 1, H - 1], K[B - 1, H - 1], V[B - 1, H - 1], 0.125, mk)
+    _check(got[B - 1, H - 1], exp, "bf16", f"{mask} {list(shape)} last head, all rows")
+    rs = np.random.default_rng(58)
+    rows = np.concatenate([[0, 255, 256, n - 1], rs.integers(0, n, size=4)])
+    err = 0.0
+    for b in range(B):
+        for i in range(H):
+            for r in rows:
+                top = r + 1 if mask == "causal" else n
+                e, _ = oracle.attention_head(Q[b, i, r:r + 1], K[b, i, :top], V[b, i, :top], 0.125)
+                err = max(err, float(np.max(np.abs(got[b, i, r] - e[0]))))
+    print(f"[parity] {mask} {list(shape)} sampled rows: max-abs {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_four_wave_workgroups_ragged_lens(dtype):
     """[8,16,1000,1000] with per-batch key lengths (0, 1, 63, 64, 500, 999,
