@@ -32,6 +32,9 @@
  *   different streams are safe as long as their buffers do not overlap.
  * - Setting the environment variable MHA_TRACE=1 logs every dispatch
  *   (kernel, grid, algorithmic bytes and flops) to stderr.
+ *   MHA_GRID_ORDER=reverse launches the attention workgroups in the opposite
+ *   order (a check that results do not depend on it; they are bitwise the
+ *   same).
  */
 #ifndef LIBMHA_MHA_H
 #define LIBMHA_MHA_H
@@ -76,8 +79,12 @@ enum {
  *   O [B, h, n_q, d_v]  (written)
  * seq_lens: NULL, or device int32[B]: batch b uses only its first
  *   seq_lens[b] keys (key padding; clamped to [0, n_k]).  Masked K/V rows
- *   are never read, so their contents (NaN included) have no effect.
- * scale: any finite float; the pages use 1/sqrt(d_k).
+ *   are never read, so their contents (NaN included) have no effect.  A
+ *   key masked for a query row (causal, window, padding) has no effect on
+ *   that row, even where its value row holds NaN or ±inf; a row that sees
+ *   such a key takes its NaN or infinity, as the formula does.
+ * scale: any finite float, or NaN for the pages' 1/sqrt(d_k) (computed by
+ *   the library in fp32); ±inf is MHA_ERR_INVALID_ARG.
  * Supported: BF16/F16 with d_k = d_v in {16, 32, 64, 128, 256, 512} and
  *   n_k·d_k·2 bytes < 2 GiB (MFMA kernels); F32 with d_k = d_v in {16, 32,
  *   64, 128}.  The head-dimension variants are those of [N] Table 3 row (A)
@@ -87,6 +94,34 @@ enum {
 int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype, int64_t B,
              int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, float scale,
              int32_t mask_kind, const int32_t* seq_lens, void* stream);
+
+/*
+ * Element strides of the four operands of mha_sdpa_strided and
+ * mha_sdpa_window_strided, each [batch, head, row] (the d axis is always
+ * contiguous).  A caller's x·W^Q of shape [B, n, h·d] viewed as [B, h, n, d]
+ * without a copy has strides {n·h·d, d, h·d} -- the head split of [M] "32
+ * Transformer" (the sketch's view and transpose of the projected rows).
+ * Strides must be >= 0 and multiples of 8 elements for BF16/F16 (4 for F32),
+ * so that every row starts on 16 bytes; 0 repeats an operand (for example one
+ * K/V head shared by all query heads).  O's strides must keep distinct
+ * (batch, head, row) on distinct elements; and with BF16/F16 a head's n_k
+ * K (V) rows must span less than 2 GiB (n_k · row stride · 2 bytes).
+ */
+typedef struct {
+  int64_t q[3], k[3], v[3], o[3];
+} mha_sdpa_strides;
+
+/*
+ * mha_sdpa on strided operands: the same computation, arguments and errors,
+ * with each operand at element (b, i, r, j) = base + b·s[0] + i·s[1] + r·s[2]
+ * + j.  O must not overlap the memory any input can touch (the span from its
+ * base to its last element), MHA_ERR_ALIAS otherwise.  strides: a host
+ * pointer, read during the call; NULL is MHA_ERR_INVALID_ARG.
+ */
+int mha_sdpa_strided(const void* Q, const void* K, const void* V, void* O,
+                     const mha_sdpa_strides* strides, int32_t dtype, int64_t B, int64_t h,
+                     int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, float scale,
+                     int32_t mask_kind, const int32_t* seq_lens, void* stream);
 
 /*
  * Restricted attention, [N] §4 (Table 1, "Auto-attention restreinte", and
@@ -103,6 +138,39 @@ int mha_sdpa_window(const void* Q, const void* K, const void* V, void* O, int32_
                     int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v,
                     float scale, int64_t left, int64_t right, const int32_t* seq_lens,
                     void* stream);
+
+/* mha_sdpa_window on strided operands, as mha_sdpa_strided. */
+int mha_sdpa_window_strided(const void* Q, const void* K, const void* V, void* O,
+                            const mha_sdpa_strides* strides, int32_t dtype, int64_t B, int64_t h,
+                            int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, float scale,
+                            int64_t left, int64_t right, const int32_t* seq_lens, void* stream);
+
+/*
+ * The kernel an attention call runs on, for the same arguments as mha_sdpa
+ * (windowed = 0) or mha_sdpa_window (windowed != 0; left, right its reaches);
+ * no device is needed.  Validation and status codes as those calls (sizes
+ * only: no pointers).  route (host) receives the kernel, its waves per
+ * workgroup, query rows per workgroup and grid size, and the mask kind the
+ * call runs with (a window that reaches every earlier key and no later one
+ * runs as the causal mask).
+ */
+enum {
+  MHA_KERNEL_F32 = 0,     /* fp32, one thread per query row                  */
+  MHA_KERNEL_BLOCKS = 1,  /* MFMA flash kernel, two 32-row blocks per wave   */
+  MHA_KERNEL_PAIRS = 2,   /* MFMA flash kernel, one 32-row block per wave,
+                             two key tiles per step                          */
+  MHA_KERNEL_SPLIT = 3,   /* MFMA flash kernel, waves split the keys         */
+  MHA_KERNEL_DECODE = 4,  /* one query row, no matrix cores                  */
+  MHA_KERNEL_WINDOW = 5,  /* MFMA flash kernel, restricted window            */
+  MHA_KERNEL_WIDE = 6     /* d_k 256, 512: waves split the head dimension    */
+};
+typedef struct {
+  int32_t kernel, waves, rows_per_workgroup, mask_kind;
+  int64_t workgroups;
+} mha_route;
+int mha_sdpa_route(int32_t dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k,
+                   int64_t d_v, int32_t mask_kind, int32_t windowed, int64_t left, int64_t right,
+                   mha_route* route);
 
 /*
  * Multi-head attention sublayer, [N] §3.2.2 ("Attention multi-têtes"):

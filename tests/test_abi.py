@@ -41,7 +41,7 @@ def test_status_strings_and_version():
         s = M.status_string(code)
         assert s.startswith("MHA_ERR_"), s
     assert "unknown" in M.status_string(-99)
-    assert M.version() == 200
+    assert M.version() == 300
 
 
 def _sdpa(dtype=M.MHA_BF16, B=1, h=1, n_q=8, n_k=8, d_k=64, d_v=64, scale=0.125,
@@ -56,8 +56,8 @@ def _sdpa(dtype=M.MHA_BF16, B=1, h=1, n_q=8, n_k=8, d_k=64, d_v=64, scale=0.125,
     (dict(B=-1), M.MHA_ERR_SHAPE),
     (dict(d_k=0), M.MHA_ERR_SHAPE),
     (dict(n_k=9, mask=M.MHA_MASK_CAUSAL), M.MHA_ERR_SHAPE),
-    (dict(scale=float("nan")), M.MHA_ERR_INVALID_ARG),
     (dict(scale=float("inf")), M.MHA_ERR_INVALID_ARG),
+    (dict(scale=float("-inf")), M.MHA_ERR_INVALID_ARG),
     (dict(d_k=1024, d_v=1024), M.MHA_ERR_UNSUPPORTED),
     (dict(d_k=256, d_v=256, dtype=M.MHA_F32), M.MHA_ERR_UNSUPPORTED),
     (dict(d_k=48, d_v=48), M.MHA_ERR_UNSUPPORTED),
@@ -86,6 +86,133 @@ def test_sdpa_alias_edges():
 def test_zero_sizes_are_noops():
     for kw in (dict(B=0), dict(h=0), dict(n_q=0), dict(B=0, Q=None, O=None)):
         assert _sdpa(**kw) == M.MHA_OK
+
+
+def test_nan_scale_means_the_default():
+    """scale NaN is the pages' 1/sqrt(d_k), resolved in the library: it passes
+    validation (a zero-size call returns OK after it) where ±inf does not."""
+    assert _sdpa(B=0, scale=float("nan")) == M.MHA_OK
+    assert _sdpa(B=0, scale=float("inf")) == M.MHA_ERR_INVALID_ARG
+
+
+def test_library_resolves_all_its_symbols():
+    """Every libmha function the library calls is defined in it (a source
+    left out of the link would show as an undefined mha symbol)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", M.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert not [ln for ln in out.splitlines() if "mha" in ln.lower()], out
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU driver is present")
+def test_valid_call_without_a_device_is_a_hip_error():
+    """On a host with no GPU a call that passes validation fails at its first
+    HIP call with MHA_ERR_HIP (and a message), not a crash.  The tensors are
+    host buffers here; with no device nothing is ever launched."""
+    import numpy as np
+    buf = np.zeros(1 << 20, dtype=np.uint8)
+    a = (buf.ctypes.data + 255) & ~255
+    L = M.lib()
+    rc = L.mha_sdpa(a, a + 65536, a + 131072, a + 196608, M.MHA_BF16, 1, 1, 8, 8, 64, 64, 0.125,
+                    M.MHA_MASK_NONE, None, None)
+    assert rc == M.MHA_ERR_HIP and "mha_sdpa" in M.last_error()
+    st = M.SdpaStrides()
+    for f in "qkvo":
+        getattr(st, f)[:] = (8 * 64, 8 * 64, 64)
+    rc = L.mha_sdpa_strided(a, a + 65536, a + 131072, a + 196608, ctypes.byref(st), M.MHA_BF16,
+                            1, 1, 8, 8, 64, 64, float("nan"), M.MHA_MASK_CAUSAL, None, None)
+    assert rc == M.MHA_ERR_HIP
+
+
+# ---- strided operands
+
+def _strided(q=(512, 512, 64), k=(512, 512, 64), v=(512, 512, 64), o=(512, 512, 64),
+             dtype=M.MHA_BF16, B=2, h=1, n_q=8, n_k=8, d=64, O=0x300000, K=0x100000, null=False):
+    st = M.SdpaStrides()
+    st.q[:], st.k[:], st.v[:], st.o[:] = q, k, v, o
+    return M.lib().mha_sdpa_strided(0x1000, K, 0x200000, O, None if null else ctypes.byref(st),
+                                    dtype, B, h, n_q, n_k, d, d, 0.125, M.MHA_MASK_NONE, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(null=True), M.MHA_ERR_INVALID_ARG),
+    (dict(q=(512, 512, -64)), M.MHA_ERR_INVALID_ARG),      # negative stride
+    (dict(k=(512, 512, 68)), M.MHA_ERR_INVALID_ARG),       # rows not on 16 bytes
+    (dict(v=(516, 512, 64)), M.MHA_ERR_INVALID_ARG),
+    (dict(o=(512, 512, 32)), M.MHA_ERR_INVALID_ARG),       # output rows overlap
+    (dict(o=(256, 512, 64)), M.MHA_ERR_INVALID_ARG),       # batches overlap
+    (dict(o=(0, 0, 64)), M.MHA_ERR_INVALID_ARG),           # batch stride 0 on the output
+    (dict(dtype=M.MHA_F32, q=(512, 512, 66)), M.MHA_ERR_INVALID_ARG),
+    (dict(k=(512, 512, 1 << 21), n_k=1024), M.MHA_ERR_UNSUPPORTED),   # K rows span > 2 GiB
+    (dict(O=0x1000 + 512 * 2 * 2 - 16), M.MHA_ERR_ALIAS),  # O starts inside Q's span
+    (dict(q=(8192, 512, 64), O=0x1000 + 8192 * 2), M.MHA_ERR_ALIAS),  # O in the gap between Q's batches
+])
+def test_strided_rejects(kw, code):
+    assert _strided(**kw) == code
+    assert M.last_error() != ""
+
+
+def test_strided_accepts_views_and_broadcast():
+    """Layouts that pass the stride checks (n_q = 0 then returns OK before any
+    pointer is used): a [B, n, h, d] view of one projected matrix as
+    [B, h, n, d], and K/V shared by every head (head stride 0)."""
+    view = (8 * 2 * 64, 64, 2 * 64)   # x·W^Q of [B, n=8, h=2, d=64] seen as [B, h, n, d]
+    assert _strided(q=view, o=view, h=2, n_q=0) == M.MHA_OK
+    assert _strided(k=(512, 0, 64), v=(512, 0, 64), o=(1024, 512, 64), h=2, n_q=0) == M.MHA_OK
+
+
+# ---- routes: which kernel each workload and each GPU test's shape runs on
+
+ROUTES = [
+    # (dtype, B, h, n_q, n_k, d, mask, window) -> (kernel, waves, workgroups or None)
+    ((M.MHA_F32, 1, 1, 16, 16, 64, "none", None), ("f32", 1, 1)),          # single head fp32
+    ((M.MHA_BF16, 32, 8, 64, 64, 64, "none", None), ("pairs", 2, 256)),    # base encoder sub-layer
+    ((M.MHA_BF16, 16, 8, 512, 512, 64, "causal", None), ("pairs", 4, 512)),  # decoder causal
+    ((M.MHA_BF16, 8, 16, 384, 512, 64, "none", None), ("pairs", 8, 256)),  # big cross-attention
+    ((M.MHA_BF16, 4, 8, 4096, 4096, 64, "none", None), ("blocks", 8, 256)),  # long, unmasked
+    ((M.MHA_BF16, 4, 8, 4096, 4096, 64, "causal", None), ("pairs", 8, 512)),  # long, causal
+    ((M.MHA_BF16, 64, 8, 1, 2048, 64, "none", None), ("decode", 8, 512)),  # decoding step
+    # shapes GPU tests rely on
+    ((M.MHA_BF16, 1, 3, 2304, 2304, 64, "causal", None), ("pairs", 4, None)),
+    ((M.MHA_BF16, 1, 4, 1536, 1536, 64, "none", None), ("pairs", 4, None)),
+    ((M.MHA_BF16, 8, 8, 2560, 2560, 64, "none", None), ("blocks", 4, None)),
+    ((M.MHA_BF16, 8, 16, 1000, 1000, 64, "none", None), ("blocks", 4, None)),
+    ((M.MHA_BF16, 8, 8, 4000, 4000, 64, "none", None), ("blocks", 8, 512)),
+    ((M.MHA_BF16, 64, 32, 50, 70, 64, "none", None), ("blocks", 1, None)),
+    ((M.MHA_BF16, 64, 32, 50, 70, 128, "none", None), ("blocks", 1, None)),
+    ((M.MHA_BF16, 8, 16, 1000, 1000, 16, "causal", None), ("blocks", 4, None)),
+    ((M.MHA_BF16, 8, 16, 1000, 1000, 128, "causal", None), ("pairs", 4, None)),
+    ((M.MHA_BF16, 8, 4, 1, 2048, 16, "none", None), ("split", 4, None)),
+    ((M.MHA_BF16, 4, 2, 4, 1000, 128, "none", None), ("split", 2, None)),
+    ((M.MHA_BF16, 1, 2, 200, 200, 32, "causal", None), ("blocks", 2, None)),
+    ((M.MHA_BF16, 1, 2, 200, 200, 512, "causal", None), ("wide", 4, 14)),
+    ((M.MHA_BF16, 8, 16, 1000, 1000, 64, "none", (128, 128)), ("window", 2, None)),
+    ((M.MHA_BF16, 8, 16, 2600, 2600, 64, "none", (1500, 600)), ("window", 4, None)),
+    ((M.MHA_BF16, 8, 16, 1000, 1000, 64, "none", (2000, 2000)), ("blocks", 4, None)),  # reaches all
+]
+
+
+@pytest.mark.parametrize("args,expect", ROUTES, ids=lambda x: "x".join(map(str, x)) if isinstance(x, tuple) else None)
+def test_route(args, expect):
+    dtype, B, h, n_q, n_k, d, mask, window = args
+    r = M.sdpa_route(dtype, B, h, n_q, n_k, d, mask=mask, window=window)
+    assert (r["kernel"], r["waves"]) == expect[:2], r
+    if expect[2] is not None:
+        assert r["workgroups"] == expect[2], r
+    assert r["rows_per_workgroup"] * r["workgroups"] >= n_q * B * h or r["kernel"] == "blocks"
+
+
+def test_route_window_forms():
+    """A window reaching every earlier key and no later one runs as the
+    causal mask; the route reports it."""
+    r = M.sdpa_route(M.MHA_BF16, 2, 2, 300, 300, 64, window=(299, 0))
+    assert r["kernel"] == "pairs" and r["mask_kind"] == M.MHA_MASK_CAUSAL
+    with pytest.raises(M.MhaError):
+        M.sdpa_route(M.MHA_BF16, 2, 2, 300, 301, 64, mask="causal")
 
 
 def _fwd(dtype=M.MHA_BF16, B=2, n_q=8, n_k=8, d_model=128, h=2, mask=M.MHA_MASK_NONE,

@@ -21,6 +21,7 @@ from transformer_head_scaled_amd import libmha, synth
 pytestmark = pytest.mark.gpu
 
 MASKS = {"none": oracle.MASK_NONE, "causal": oracle.MASK_CAUSAL}
+_TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -63,40 +64,37 @@ def test_workload_causal_b16_n512(dtype):
 
 
 @pytest.mark.parametrize("mask", ["none", "causal"])
-def test_workload_long_b4_n4096_sampled(mask):
-    """[4,8,4096,64], the launch the bench times: two whole heads, plus 12
-    sampled rows (first, last, random) of every head."""
+def test_workload_long_b4_n4096_all_heads(mask):
+    """[4,8,4096,64], the launch the bench times: every output of every one
+    of the 32 heads against the oracle."""
     dtype = "bf16"
     ins = synth.sdpa_inputs(5, 4, 8, 4096, 4096, 64, dtype=dtype)
     note(f"sdpa bf16 {mask} [4,8,4096,64]")
     got = _run(ins, dtype, mask)
     Q, K, V = (ins[n][1] for n in "QKV")
     mk = MASKS[mask]
-    for (b, i) in ((0, 0), (3, 7)):
-        exp, _ = oracle.attention_head(Q[b, i], K[b, i], V[b, i], 0.125, mk)
-        _check(got[b, i], exp, dtype, f"{mask} head ({b},{i}) all rows")
-    rs = np.random.default_rng(55)
-    rows = np.concatenate([[0, 1, 63, 64, 4095], rs.integers(0, 4096, size=7)])
     err = 0.0
     for b in range(4):
         for i in range(8):
-            for r in rows:
-                top = r + 1 if mask == "causal" else 4096
-                exp, _ = oracle.attention_head(Q[b, i, r:r + 1], K[b, i, :top], V[b, i, :top], 0.125)
-                err = max(err, float(np.max(np.abs(got[b, i, r] - exp[0]))))
-    print(f"[parity] {mask} sampled rows of all heads: max-abs {err:.3e}", flush=True)
+            exp, _ = oracle.attention_head(Q[b, i], K[b, i], V[b, i], 0.125, mk)
+            assert np.all(np.isfinite(got[b, i])), f"head ({b},{i}): non-finite output"
+            err = max(err, float(np.max(np.abs(got[b, i] - exp))))
+    print(f"[parity] {mask} [4,8,4096,64] all 32 heads: max-abs {err:.3e}", flush=True)
     assert err <= TOL[dtype]
 
 
-@pytest.mark.parametrize("shape,mask", [
-    ((1, 3, 2304, 64), "causal"),   # few heads: four-wave pair workgroups past 2048 rows
-    ((1, 4, 1536, 64), "none"),     # unmasked pair layout, four waves by the makespan rule
-    ((8, 8, 2560, 64), "none"),     # two-block layout, four waves (ragged eight-wave round)
+@pytest.mark.parametrize("shape,mask,route", [
+    ((1, 3, 2304, 64), "causal", ("pairs", 4)),   # few heads: four-wave pair workgroups past 2048 rows
+    ((1, 4, 1536, 64), "none", ("pairs", 4)),     # unmasked pair layout, four waves by the makespan rule
+    ((8, 8, 2560, 64), "none", ("blocks", 4)),    # two-block layout, four waves (ragged eight-wave round)
 ])
-def test_workgroup_size_rules_sampled(shape, mask):
+def test_workgroup_size_rules_sampled(shape, mask, route):
     """Shapes whose workgroup size comes from the grid-size rules (few heads,
-    ragged last rounds): one whole head, plus sampled rows of every head."""
+    ragged last rounds; the route is asserted): one whole head, plus sampled
+    rows of every head."""
     B, H, n, d = shape
+    r = libmha.sdpa_route(libmha.MHA_BF16, B, H, n, n, d, mask=mask)
+    assert (r["kernel"], r["waves"]) == route, r
     ins = synth.sdpa_inputs(57, B, H, n, n, d, dtype="bf16")
     note(f"sdpa bf16 {mask} {list(shape)}")
     got = _run(ins, "bf16", mask)
@@ -137,17 +135,19 @@ def test_four_wave_workgroups_ragged_lens(dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_eight_wave_workgroups_ragged_lens(dtype):
-    """[8,16,2100,2100] unmasked with key lengths (0, 1, 63, 64, 1000, 2099,
-    2100, and one past n_k): 2048 query rows or more take 8-wave (512-row)
-    workgroups, here with a ragged last one and key-length boundary tiles.
-    One whole head per batch is compared."""
-    lens = [2100, 2099, 1000, 64, 63, 1, 0, 3000]
-    ins = synth.sdpa_inputs(37, 8, 16, 2100, 2100, 64, dtype=dtype)
-    note(f"sdpa {dtype} [8,16,2100,2100] key lengths {lens}")
+    """[8,8,4000,4000] unmasked with key lengths (0, 1, 63, 64, 1000, 3999,
+    4000, and one past n_k): the two-block layout with eight-wave (512-row)
+    workgroups (the route is asserted), a ragged last one (4000 = 7·512 +
+    416) and key-length boundary tiles.  One whole head per batch."""
+    lens = [4000, 3999, 1000, 64, 63, 1, 0, 5000]
+    r = libmha.sdpa_route(libmha.dtype_code(torch.empty(0, dtype=_TORCH[dtype])), 8, 8, 4000, 4000, 64)
+    assert (r["kernel"], r["waves"]) == ("blocks", 8), r
+    ins = synth.sdpa_inputs(37, 8, 8, 4000, 4000, 64, dtype=dtype)
+    note(f"sdpa {dtype} [8,8,4000,4000] key lengths {lens}")
     got = _run(ins, dtype, "none", lens)
     Q, K, V = (ins[n][1] for n in "QKV")
     for b in range(8):
-        i = (3 * b + 2) % 16
+        i = (3 * b + 2) % 8
         exp = oracle.sdpa(Q[b:b + 1, i:i + 1], K[b:b + 1, i:i + 1], V[b:b + 1, i:i + 1], 0.125,
                           oracle.MASK_NONE, [lens[b]])[0, 0]
         _check(got[b, i], exp, dtype, f"{dtype} 8-wave head ({b},{i}) len {lens[b]}")
@@ -290,23 +290,85 @@ DECODE_CASES = [
 ]
 
 
-def test_causal_nan_values_past_a_waves_rows():
-    """Causal [1,2,200,200] (two-wave workgroups, each wave a pair of 32-row
-    blocks) with the value rows 160.. set to NaN: rows below 160 never see
-    them, and the wave whose highest block ends at row 159 loads keys
-    160..191 with its diagonal tile -- their weights are 0 and their values
-    are cleared before P·V, so those rows stay finite and exact."""
-    ins = synth.sdpa_inputs(47, 1, 2, 200, 200, 64, dtype="bf16")
-    Vst = ins["V"][0].copy()
-    Vst.view(np.uint16)[:, :, 160:] = 0x7fc0  # bf16 NaN
-    tq, tk = (to_dev(ins[n][0], "bf16") for n in "QK")
-    tv = to_dev(Vst, "bf16")
-    note("sdpa bf16 causal [1,2,200,200] NaN values past row 159")
-    out = libmha.sdpa(tq, tk, tv, scale=0.125, mask="causal")
+# Non-finite value rows inside masked tiles.  A masked key's weight is
+# exactly 0, so its value row must have no effect even when it holds NaN or
+# ±inf, while a row that does see the key takes its NaN or infinity.  The
+# special keys sit inside 32-row blocks (not on block or tile boundaries), so
+# that rows of the same block on either side of the key load it with their
+# diagonal (or window-edge) tile; they fall in the tiles where both blocks
+# of a wave are masked (key 40), where one block is (170, 183), and in the
+# middle of a window edge (101).  Each key holds a different mix of NaN, +inf
+# and -inf columns, so rows that see several keys get NaN from inf - inf.
+NONFINITE_KEYS = {40: {5: "nan", 6: "inf"}, 101: {1: "-inf"}, 170: {0: "nan", 2: "inf", 3: "inf"},
+                  183: {2: "-inf", 3: "inf", 7: "nan"}}
+
+
+def _plant_nonfinite(ins, dtype, d):
+    """Write the special values into the stored V (and its float64 copy)."""
+    bits = {"bf16": {"nan": 0x7fc0, "inf": 0x7f80, "-inf": 0xff80},
+            "f16": {"nan": 0x7e00, "inf": 0x7c00, "-inf": 0xfc00}}
+    val = {"nan": np.nan, "inf": np.inf, "-inf": -np.inf}
+    st, v64 = ins["V"][0], ins["V"][1]
+    for key, cols in NONFINITE_KEYS.items():
+        for col, kind in cols.items():
+            j = col % d
+            if dtype == "f32":
+                st[:, :, key, j] = np.float32(val[kind])
+            else:
+                st.view(np.uint16)[:, :, key, j] = bits[dtype][kind]
+            v64[:, :, key, j] = val[kind]
+
+
+def _check_nonfinite(got, exp, dtype, what):
+    """NaN exactly where the oracle has NaN, the same infinities, and the
+    finite outputs within the tolerance."""
+    assert np.array_equal(np.isnan(got), np.isnan(exp)), f"{what}: NaN positions differ"
+    inf = np.isinf(exp)
+    assert np.array_equal(np.isinf(got), inf) and np.array_equal(got[inf], exp[inf]), \
+        f"{what}: infinities differ"
+    fin = np.isfinite(exp)
+    err = float(np.max(np.abs(got[fin] - exp[fin])))
+    n_bad = int((~fin).sum())
+    print(f"[parity] {what}: {n_bad} non-finite outputs match, finite max-abs {err:.3e}", flush=True)
+    assert n_bad > 0 and err <= TOL[dtype], f"{what}: max-abs {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128, 256, 512])
+def test_nonfinite_values_inside_masked_tiles(dtype, d):
+    """Causal [1,2,200,200] (and key lengths 200, 190) with NaN/±inf value
+    elements at keys 40, 101, 170, 183: every output row against the oracle,
+    NaN and infinities included.  Covers the two-block layout (d 16, 32),
+    the pair layout (d 64, 128), the wide-head kernel (d 256, 512) and the
+    fp32 kernel."""
+    if dtype == "f32" and d > 128:
+        pytest.skip("the fp32 path stops at d 128")
+    scale = 1 / math.sqrt(d)
+    for lens in (None, [200, 190]):
+        B = 1 if lens is None else 2
+        ins = synth.sdpa_inputs(47 + d, B, 2, 200, 200, d, dtype=dtype)
+        _plant_nonfinite(ins, dtype, d)
+        note(f"sdpa {dtype} d={d} causal [{B},2,200,200] non-finite values, lens {lens}")
+        got = _run(ins, dtype, "causal", lens, scale=scale)
+        exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], scale, oracle.MASK_CAUSAL, lens)
+        _check_nonfinite(got, exp, dtype, f"{dtype} d={d} causal non-finite values lens {lens}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [16, 64, 128])
+def test_nonfinite_values_window_edges(dtype, d):
+    """Restricted attention over [1,2,200,200] (reach 37 back, 5 forward)
+    with the same non-finite value elements: each special key lies inside
+    the windows of some rows of its block and outside those of others."""
+    scale = 1 / math.sqrt(d)
+    ins = synth.sdpa_inputs(53 + d, 1, 2, 200, 200, d, dtype=dtype)
+    _plant_nonfinite(ins, dtype, d)
+    tq, tk, tv = (to_dev(ins[n][0], dtype) for n in "QKV")
+    note(f"sdpa_window {dtype} d={d} [1,2,200,200] (37, 5) non-finite values")
+    out = libmha.sdpa_window(tq, tk, tv, 37, 5, scale=scale)
     torch.cuda.synchronize()
-    got = from_dev(out)[:, :, :160]
-    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], 0.125, oracle.MASK_CAUSAL)[:, :, :160]
-    _check(got, exp, "bf16", "causal rows < 160 with NaN values past them")
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], scale, window=(37, 5))
+    _check_nonfinite(from_dev(out), exp, dtype, f"{dtype} d={d} window non-finite values")
 
 
 def test_workload_decode_step():

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libmha.so")
-SOURCES = ["mha_api.cpp", "sdpa_fwd.hip", "sdpa_window.hip", "sdpa_wide.hip", "sdpa_decode.hip",
+SOURCES = ["mha_api.cpp", "sdpa_route.cpp", "sdpa_fwd.hip", "sdpa_window.hip", "sdpa_wide.hip", "sdpa_decode.hip",
            "gemm_proj.hip", "add_norm.hip"]
 # Per-source flags.  The flash attention kernel is scheduled with LLVM's
 # "max-memory-clause" strategy: the same instructions and results, measured

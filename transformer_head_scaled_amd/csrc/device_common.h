@@ -66,6 +66,28 @@ __device__ __forceinline__ f32x4 unpack4(u32x2 w) {
   }
 }
 
+// Non-finite half-precision values.  A 16-bit value is NaN or ±inf exactly
+// when its magnitude bits (sign cleared) reach the all-ones exponent:
+// 0x7f80 for bf16, 0x7c00 for fp16.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+template <int DT>
+__device__ __forceinline__ constexpr unsigned short nonfinite_from() {
+  return DT == DT_BF16 ? 0x7f80 : 0x7c00;
+}
+// Running per-half maximum of the magnitude bits of packed words (two
+// instructions per word: an AND and a packed 16-bit max).
+__device__ __forceinline__ u16x2 magnitude_max(u16x2 acc, uint32_t w) {
+  return __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, w & 0x7fff7fffu));
+}
+// A packed word with its non-finite halves replaced by +0.
+template <int DT>
+__device__ __forceinline__ uint32_t zero_nonfinite(uint32_t w) {
+  constexpr uint32_t lim = nonfinite_from<DT>();
+  const uint32_t lo = (w & 0x7fffu) >= lim ? 0u : 0x0000ffffu;
+  const uint32_t hi = ((w >> 16) & 0x7fffu) >= lim ? 0u : 0xffff0000u;
+  return w & (lo | hi);
+}
+
 // Sign bit of each 16-bit lane of a packed word (used to negate operands
 // exactly).
 __device__ __forceinline__ u32x4 flip_signs(u32x4 v) {

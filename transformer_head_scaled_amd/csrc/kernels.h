@@ -25,18 +25,43 @@ struct SdpaArgs {
   // r - win_left <= c <= r + win_right (window != 0; reaches clamped to
   // [0, n_q] and [0, n_k])
   int32_t window, win_left, win_right;
+  // launch the workgroups in the opposite order (the flash kernel; the
+  // results are the same, which the determinism tests check)
+  int32_t reverse;
 };
 
-hipError_t launch_sdpa(const SdpaArgs& a, int dtype, int causal, int d, float scale, hipStream_t st);
+// The attention kernel a problem runs on, and its workgroup shape
+// (sdpa_route.cpp).  The values are those of MHA_KERNEL_* in mha.h.
+enum SdpaKernel : int {
+  SDPA_K_F32 = 0,     // fp32 kernel
+  SDPA_K_BLOCKS = 1,  // flash kernel, two 32-row blocks a wave
+  SDPA_K_PAIRS = 2,   // flash kernel, one 32-row block a wave, two key tiles a step
+  SDPA_K_SPLIT = 3,   // flash kernel, the waves of a workgroup split the keys
+  SDPA_K_DECODE = 4,  // one query row, registers only
+  SDPA_K_WINDOW = 5,  // flash kernel, restricted window
+  SDPA_K_WIDE = 6     // d = 256, 512: the waves of a workgroup split d
+};
+struct SdpaRoute {
+  int kernel;          // SdpaKernel
+  int waves;           // waves per workgroup
+  int rows;            // query rows per workgroup
+  int64_t workgroups;  // grid size
+};
+// win_left / win_right: the reaches after clamping to [0, n_q] and [0, n_k]
+SdpaRoute sdpa_route(int dtype, bool causal, bool window, int64_t B, int64_t H, int64_t n_q,
+                     int64_t n_k, int d, int64_t win_left, int64_t win_right);
+
+// Launch what the route names (errors if the route does not fit the
+// arguments).
+hipError_t launch_sdpa(const SdpaArgs& a, const SdpaRoute& r, int dtype, int causal, int d,
+                       float scale, hipStream_t st);
 // the flash kernel's window form (bf16 / fp16), sdpa_window.hip
-hipError_t launch_sdpa_window(const SdpaArgs& a, int dtype, int d, hipStream_t st);
+hipError_t launch_sdpa_window(const SdpaArgs& a, const SdpaRoute& r, int dtype, int d, hipStream_t st);
 // wide heads, d = 256 or 512 (bf16 / fp16, no window), sdpa_wide.hip
 hipError_t launch_sdpa_wide(const SdpaArgs& a, int dtype, int causal, int d, hipStream_t st);
 // one query row against a long key/value cache (bf16 / fp16, d = 64, 128,
 // no mask but key lengths), sdpa_decode.hip
-bool sdpa_decode_applies(const SdpaArgs& a, int dtype, int causal, int d);
 hipError_t launch_sdpa_decode(const SdpaArgs& a, int dtype, int d, hipStream_t st);
-int sdpa_rows_per_workgroup(int dtype, int causal, int64_t n_q, int64_t n_k, int64_t heads, int d);
 
 // One GEMM C = A·W of the projections: A [M, K] row-major (row stride lda),
 // W [K, N] row-major (row stride ldw).  Output element (m, n) is written to

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <utility>
 
 #include "kernels.h"
 
@@ -111,102 +112,182 @@ const char* mha_status_string(int status) {
 
 const char* mha_last_error(void) { return g_err; }
 
-int mha_version(void) { return 200; }
+int mha_version(void) { return 300; }
 
-// mha_sdpa and mha_sdpa_window: with `window`, key c is visible to query r
-// iff r - left <= c <= r + right.
-static int sdpa_impl(const char* fn, const void* Q, const void* K, const void* V, void* O,
-                     int32_t dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k,
-                     int64_t d_v, float scale, int32_t mask_kind, bool window, int64_t left,
-                     int64_t right, const int32_t* seq_lens, void* stream) {
-  if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16)
-    return fail(MHA_ERR_DTYPE, "%s: dtype %d", fn, (int)dtype);
-  if (mask_kind != MHA_MASK_NONE && mask_kind != MHA_MASK_CAUSAL)
-    return fail(MHA_ERR_INVALID_ARG, "%s: mask_kind %d", fn, (int)mask_kind);
-  if (B < 0 || h < 0 || n_q < 0 || n_k < 0 || d_k <= 0 || d_v <= 0)
+// The sizes of one attention call, validated (dtype, shapes, scale, window)
+// and brought to the form the launch uses: a NaN scale becomes 1/sqrt(d_k), a
+// window that reaches every key is dropped, and one that reaches every
+// earlier key and no later one becomes the causal mask.
+struct SdpaSizes {
+  int32_t dtype;
+  int64_t B, h, n_q, n_k, d_k, d_v;
+  float scale;
+  int32_t mask_kind;
+  bool window;
+  int64_t left, right;  // reaches, clamped to [0, n_q] and [0, n_k]
+};
+
+static int sdpa_sizes(const char* fn, SdpaSizes& z) {
+  if (z.dtype != MHA_F32 && z.dtype != MHA_BF16 && z.dtype != MHA_F16)
+    return fail(MHA_ERR_DTYPE, "%s: dtype %d", fn, (int)z.dtype);
+  if (z.mask_kind != MHA_MASK_NONE && z.mask_kind != MHA_MASK_CAUSAL)
+    return fail(MHA_ERR_INVALID_ARG, "%s: mask_kind %d", fn, (int)z.mask_kind);
+  if (z.B < 0 || z.h < 0 || z.n_q < 0 || z.n_k < 0 || z.d_k <= 0 || z.d_v <= 0)
     return fail(MHA_ERR_SHAPE, "%s: negative or zero size", fn);
-  if (n_q > kMaxRows || n_k > kMaxRows || B > 65535 || h > 65535 || B * h > (int64_t)1 << 24)
+  if (z.n_q > kMaxRows || z.n_k > kMaxRows || z.B > 65535 || z.h > 65535 || z.B * z.h > (int64_t)1 << 24)
     return fail(MHA_ERR_SHAPE, "%s: size beyond the supported range", fn);
-  if (mask_kind == MHA_MASK_CAUSAL && n_q != n_k)
+  if (z.mask_kind == MHA_MASK_CAUSAL && z.n_q != z.n_k)
     return fail(MHA_ERR_SHAPE, "%s: causal mask needs n_q == n_k (%lld vs %lld)", fn,
-                (long long)n_q, (long long)n_k);
-  if (!std::isfinite(scale)) return fail(MHA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
-  if (window && (left < 0 || right < 0))
+                (long long)z.n_q, (long long)z.n_k);
+  // NaN: the pages' scale 1/sqrt(d_k)
+  if (std::isnan(z.scale)) z.scale = 1.0f / std::sqrt((float)z.d_k);
+  if (!std::isfinite(z.scale)) return fail(MHA_ERR_INVALID_ARG, "%s: scale is infinite", fn);
+  if (z.window && (z.left < 0 || z.right < 0))
     return fail(MHA_ERR_INVALID_ARG, "%s: window reaches must be >= 0 (%lld, %lld)", fn,
-                (long long)left, (long long)right);
-  // a window that reaches every key is no restriction; one that reaches every
-  // earlier key and no later one is the causal mask
-  if (window && left >= n_q - 1 && right >= n_k - 1) window = false;
-  if (window && left >= n_q - 1 && right == 0 && n_q == n_k) {
-    window = false;
-    mask_kind = MHA_MASK_CAUSAL;
+                (long long)z.left, (long long)z.right);
+  if (z.window && z.left >= z.n_q - 1 && z.right >= z.n_k - 1) z.window = false;
+  if (z.window && z.left >= z.n_q - 1 && z.right == 0 && z.n_q == z.n_k) {
+    z.window = false;
+    z.mask_kind = MHA_MASK_CAUSAL;
   }
-  if (dtype == MHA_F32) {
-    if (d_k != d_v || (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128))
+  if (!z.window) z.left = z.right = 0;
+  if (z.left > z.n_q) z.left = z.n_q;
+  if (z.right > z.n_k) z.right = z.n_k;
+  const int64_t d = z.d_k;
+  if (z.dtype == MHA_F32) {
+    if (z.d_k != z.d_v || (d != 16 && d != 32 && d != 64 && d != 128))
       return fail(MHA_ERR_UNSUPPORTED, "%s: f32 needs d_k == d_v in {16,32,64,128}", fn);
-  } else if (d_k != d_v || (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128 && d_k != 256 &&
-                            d_k != 512)) {
+  } else if (z.d_k != z.d_v || (d != 16 && d != 32 && d != 64 && d != 128 && d != 256 && d != 512)) {
     return fail(MHA_ERR_UNSUPPORTED, "%s: bf16/f16 needs d_k == d_v in {16,32,64,128,256,512}", fn);
-  } else if (window && d_k > 128) {
+  } else if (z.window && d > 128) {
     return fail(MHA_ERR_UNSUPPORTED, "%s: the window needs d_k <= 128", fn);
-  } else if (n_k * d_k * 2 > kMaxBufferBytes) {
-    return fail(MHA_ERR_UNSUPPORTED, "%s: one head's K/V exceeds 2 GiB (n_k %lld)", fn,
-                (long long)n_k);
   }
+  return MHA_OK;
+}
+
+static mha::SdpaRoute route_of(const SdpaSizes& z) {
+  return mha::sdpa_route(z.dtype, z.mask_kind == MHA_MASK_CAUSAL, z.window, z.B, z.h, z.n_q, z.n_k,
+                         (int)z.d_k, z.left, z.right);
+}
+
+// One [B, h, n, d] operand: element strides of batch, head and row (the d
+// axis contiguous).
+struct Operand {
+  const void* p;
+  int64_t sb, sh, sr;
+  int64_t n, d;
+};
+
+// [lo, hi) bytes an operand can touch
+static Range span_of(const Operand& t, int64_t B, int64_t h, size_t es) {
+  const int64_t last = t.sb * (B - 1) + t.sh * (h - 1) + t.sr * (t.n - 1) + t.d;
+  return range_of(t.p, (size_t)last * es);
+}
+
+// Distinct (batch, head, row) of an output land on distinct elements: the
+// dimensions, ordered by stride, each step past everything inside the
+// previous ones.
+static bool rows_disjoint(const Operand& o, int64_t B, int64_t h) {
+  struct Dim { int64_t stride, size; } dims[3] = {{o.sr, o.n}, {o.sh, h}, {o.sb, B}};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (dims[j].stride < dims[i].stride) std::swap(dims[i], dims[j]);
+  int64_t extent = o.d;  // elements spanned by the dimensions so far
+  for (const Dim& dm : dims) {
+    if (dm.size <= 1) continue;
+    if (dm.stride < extent) return false;
+    extent = dm.stride * (dm.size - 1) + extent;
+  }
+  return true;
+}
+
+static bool reverse_grid() {
+  const char* e = std::getenv("MHA_GRID_ORDER");
+  return e && std::strcmp(e, "reverse") == 0;
+}
+
+// mha_sdpa, mha_sdpa_window and their strided forms.  st: element strides
+// ([batch, head, row] of Q, K, V, O), or NULL for contiguous tensors.
+static int sdpa_impl(const char* fn, const void* Q, const void* K, const void* V, void* O,
+                     const mha_sdpa_strides* st, SdpaSizes z, const int32_t* seq_lens,
+                     void* stream) {
+  int rc = sdpa_sizes(fn, z);
+  if (rc != MHA_OK) return rc;
+  const int64_t B = z.B, h = z.h, n_q = z.n_q, n_k = z.n_k, d_k = z.d_k, d_v = z.d_v;
+  Operand q{Q, h * n_q * d_k, n_q * d_k, d_k, n_q, d_k}, k{K, h * n_k * d_k, n_k * d_k, d_k, n_k, d_k},
+      v{V, h * n_k * d_v, n_k * d_v, d_v, n_k, d_v}, o{O, h * n_q * d_v, n_q * d_v, d_v, n_q, d_v};
+  const size_t es = elem_size(z.dtype);
+  if (st) {
+    Operand* ops[4] = {&q, &k, &v, &o};
+    const int64_t* s3[4] = {st->q, st->k, st->v, st->o};
+    const int64_t align = 16 / (int64_t)es;  // rows start on 16 bytes
+    for (int i = 0; i < 4; ++i) {
+      for (int j = 0; j < 3; ++j)
+        if (s3[i][j] < 0 || s3[i][j] % align != 0)
+          return fail(MHA_ERR_INVALID_ARG,
+                      "%s: strides must be >= 0 and multiples of %lld elements (operand %d, stride %lld)",
+                      fn, (long long)align, i, (long long)s3[i][j]);
+      ops[i]->sb = s3[i][0], ops[i]->sh = s3[i][1], ops[i]->sr = s3[i][2];
+    }
+    if (!rows_disjoint(o, B, h))
+      return fail(MHA_ERR_INVALID_ARG, "%s: O strides make output rows overlap", fn);
+  }
+  if (z.dtype != MHA_F32 && n_k > 0 &&
+      (n_k * k.sr * (int64_t)es > kMaxBufferBytes || n_k * v.sr * (int64_t)es > kMaxBufferBytes))
+    return fail(MHA_ERR_UNSUPPORTED, "%s: one head's K/V rows span more than 2 GiB (n_k %lld)", fn,
+                (long long)n_k);
   if (B == 0 || h == 0 || n_q == 0) return ok();
   if (!Q || !O || ((!K || !V) && n_k > 0))
     return fail(MHA_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3) != 0)
     return fail(MHA_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
-  const size_t es = elem_size(dtype);
-  const Range ro = range_of(O, (size_t)(B * h * n_q * d_v) * es);
-  if (overlap(ro, range_of(Q, (size_t)(B * h * n_q * d_k) * es)) ||
-      overlap(ro, range_of(K, (size_t)(B * h * n_k * d_k) * es)) ||
-      overlap(ro, range_of(V, (size_t)(B * h * n_k * d_v) * es)) ||
+  const Range ro = span_of(o, B, h, es);
+  if (overlap(ro, span_of(q, B, h, es)) || (n_k > 0 && overlap(ro, span_of(k, B, h, es))) ||
+      (n_k > 0 && overlap(ro, span_of(v, B, h, es))) ||
       (seq_lens && overlap(ro, range_of(seq_lens, (size_t)B * 4))))
     return fail(MHA_ERR_ALIAS, "%s: O overlaps an input", fn);
 
   mha::SdpaArgs a{};
-  a.Q = Q;
-  a.K = K;
-  a.V = V;
-  a.O = O;
-  a.q_sr = d_k, a.q_sh = n_q * d_k, a.q_sb = h * n_q * d_k;
-  a.k_sr = d_k, a.k_sh = n_k * d_k, a.k_sb = h * n_k * d_k;
-  a.v_sr = d_v, a.v_sh = n_k * d_v, a.v_sb = h * n_k * d_v;
-  a.o_sr = d_v, a.o_sh = n_q * d_v, a.o_sb = h * n_q * d_v;
+  a.Q = Q, a.K = K, a.V = V, a.O = O;
+  a.q_sb = q.sb, a.q_sh = q.sh, a.q_sr = q.sr;
+  a.k_sb = k.sb, a.k_sh = k.sh, a.k_sr = k.sr;
+  a.v_sb = v.sb, a.v_sh = v.sh, a.v_sr = v.sr;
+  a.o_sb = o.sb, a.o_sh = o.sh, a.o_sr = o.sr;
   a.B = (int32_t)B, a.H = (int32_t)h, a.n_q = (int32_t)n_q, a.n_k = (int32_t)n_k;
   // c is clamped away from 0: for |scale| this small every visible weight
   // is exp2(~0) = 1 in fp32 (the uniform softmax scale 0 defines), while
   // masked scores (-inf) still give exactly 0
-  a.c = std::fmax(std::fabs(scale) * 1.4426950408889634f, 1e-30f);
-  a.neg = scale < 0.f ? 1 : 0;
+  a.c = std::fmax(std::fabs(z.scale) * 1.4426950408889634f, 1e-30f);
+  a.neg = z.scale < 0.f ? 1 : 0;
   a.lens = seq_lens;
-  a.window = window ? 1 : 0;
-  a.win_left = (int32_t)(left < n_q ? left : n_q);
-  a.win_right = (int32_t)(right < n_k ? right : n_k);
+  a.window = z.window ? 1 : 0;
+  a.win_left = (int32_t)z.left;
+  a.win_right = (int32_t)z.right;
+  a.reverse = reverse_grid() ? 1 : 0;
+  const mha::SdpaRoute r = route_of(z);
   if (trace_on()) {
-    double vis = mask_kind == MHA_MASK_CAUSAL ? 0.5 * n_q * (n_q + 1) : (double)n_q * n_k;
-    if (window) {
+    double vis = z.mask_kind == MHA_MASK_CAUSAL ? 0.5 * n_q * (n_q + 1) : (double)n_q * n_k;
+    if (z.window) {
       vis = 0.0;
-      for (int64_t r = 0; r < n_q; ++r) {
-        const int64_t lo = r - a.win_left > 0 ? r - a.win_left : 0;
-        const int64_t hi = r + a.win_right < n_k - 1 ? r + a.win_right : n_k - 1;
+      for (int64_t row = 0; row < n_q; ++row) {
+        const int64_t lo = row - z.left > 0 ? row - z.left : 0;
+        const int64_t hi = row + z.right < n_k - 1 ? row + z.right : n_k - 1;
         if (hi >= lo) vis += (double)(hi - lo + 1);
       }
     }
     std::fprintf(stderr,
-                 "[libmha] %s dtype=%d B=%lld h=%lld n_q=%lld n_k=%lld d=%lld mask=%d window=%d,%d "
-                 "lens=%s rows/wg=%d flops(visible)=%.4g bytes=%.4g\n",
-                 fn, (int)dtype, (long long)B, (long long)h, (long long)n_q, (long long)n_k,
-                 (long long)d_k, (int)mask_kind, window ? a.win_left : -1, window ? a.win_right : -1,
-                 seq_lens ? "yes" : "no",
-                 mha::sdpa_rows_per_workgroup(dtype, mask_kind == MHA_MASK_CAUSAL, n_q, n_k, B * h, (int)d_k), 4.0 * d_k * vis * B * h,
+                 "[libmha] %s dtype=%d B=%lld h=%lld n_q=%lld n_k=%lld d=%lld mask=%d window=%lld,%lld "
+                 "lens=%s strided=%d kernel=%d waves=%d rows/wg=%d wgs=%lld flops(visible)=%.4g "
+                 "bytes=%.4g\n",
+                 fn, (int)z.dtype, (long long)B, (long long)h, (long long)n_q, (long long)n_k,
+                 (long long)d_k, (int)z.mask_kind, z.window ? (long long)z.left : -1LL,
+                 z.window ? (long long)z.right : -1LL, seq_lens ? "yes" : "no", st ? 1 : 0, r.kernel,
+                 r.waves, r.rows, (long long)r.workgroups, 4.0 * d_k * vis * B * h,
                  (double)es * B * h * (2 * n_q * d_k + 2 * n_k * d_k));
   }
-  const hipError_t e = mha::launch_sdpa(a, dtype, mask_kind == MHA_MASK_CAUSAL, (int)d_k, scale,
-                                        (hipStream_t)stream);
+  const hipError_t e = mha::launch_sdpa(a, r, z.dtype, z.mask_kind == MHA_MASK_CAUSAL, (int)d_k,
+                                        z.scale, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
 }
@@ -214,16 +295,54 @@ static int sdpa_impl(const char* fn, const void* Q, const void* K, const void* V
 int mha_sdpa(const void* Q, const void* K, const void* V, void* O, int32_t dtype, int64_t B,
              int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, float scale,
              int32_t mask_kind, const int32_t* seq_lens, void* stream) {
-  return sdpa_impl("mha_sdpa", Q, K, V, O, dtype, B, h, n_q, n_k, d_k, d_v, scale, mask_kind,
-                   false, 0, 0, seq_lens, stream);
+  return sdpa_impl("mha_sdpa", Q, K, V, O, nullptr,
+                   SdpaSizes{dtype, B, h, n_q, n_k, d_k, d_v, scale, mask_kind, false, 0, 0},
+                   seq_lens, stream);
+}
+
+int mha_sdpa_strided(const void* Q, const void* K, const void* V, void* O,
+                     const mha_sdpa_strides* strides, int32_t dtype, int64_t B, int64_t h,
+                     int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, float scale,
+                     int32_t mask_kind, const int32_t* seq_lens, void* stream) {
+  if (!strides) return fail(MHA_ERR_INVALID_ARG, "mha_sdpa_strided: null strides");
+  return sdpa_impl("mha_sdpa_strided", Q, K, V, O, strides,
+                   SdpaSizes{dtype, B, h, n_q, n_k, d_k, d_v, scale, mask_kind, false, 0, 0},
+                   seq_lens, stream);
 }
 
 int mha_sdpa_window(const void* Q, const void* K, const void* V, void* O, int32_t dtype,
                     int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v,
                     float scale, int64_t left, int64_t right, const int32_t* seq_lens,
                     void* stream) {
-  return sdpa_impl("mha_sdpa_window", Q, K, V, O, dtype, B, h, n_q, n_k, d_k, d_v, scale,
-                   MHA_MASK_NONE, true, left, right, seq_lens, stream);
+  return sdpa_impl("mha_sdpa_window", Q, K, V, O, nullptr,
+                   SdpaSizes{dtype, B, h, n_q, n_k, d_k, d_v, scale, MHA_MASK_NONE, true, left, right},
+                   seq_lens, stream);
+}
+
+int mha_sdpa_window_strided(const void* Q, const void* K, const void* V, void* O,
+                            const mha_sdpa_strides* strides, int32_t dtype, int64_t B, int64_t h,
+                            int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, float scale,
+                            int64_t left, int64_t right, const int32_t* seq_lens, void* stream) {
+  if (!strides) return fail(MHA_ERR_INVALID_ARG, "mha_sdpa_window_strided: null strides");
+  return sdpa_impl("mha_sdpa_window_strided", Q, K, V, O, strides,
+                   SdpaSizes{dtype, B, h, n_q, n_k, d_k, d_v, scale, MHA_MASK_NONE, true, left, right},
+                   seq_lens, stream);
+}
+
+int mha_sdpa_route(int32_t dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k,
+                   int64_t d_v, int32_t mask_kind, int32_t windowed, int64_t left, int64_t right,
+                   mha_route* route) {
+  if (!route) return fail(MHA_ERR_INVALID_ARG, "mha_sdpa_route: null route");
+  SdpaSizes z{dtype, B, h, n_q, n_k, d_k, d_v, 1.f, mask_kind, windowed != 0, left, right};
+  const int rc = sdpa_sizes("mha_sdpa_route", z);
+  if (rc != MHA_OK) return rc;
+  const mha::SdpaRoute r = route_of(z);
+  route->kernel = r.kernel;
+  route->waves = r.waves;
+  route->rows_per_workgroup = r.rows;
+  route->mask_kind = z.mask_kind;
+  route->workgroups = (B == 0 || h == 0 || n_q == 0) ? 0 : r.workgroups;
+  return ok();
 }
 
 size_t mha_forward_workspace_size(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model,
@@ -362,7 +481,9 @@ static int forward_impl(const char* fn, const void* x_q, const void* x_kv, const
     a.c = scale * 1.4426950408889634f;
     a.neg = 0;
     a.lens = kv_lens;
-    e = mha::launch_sdpa(a, dtype, mask_kind == MHA_MASK_CAUSAL, (int)d, scale, st);
+    const mha::SdpaRoute r = mha::sdpa_route(dtype, mask_kind == MHA_MASK_CAUSAL, false, B, h, n_q,
+                                             n_k, (int)d, 0, 0);
+    e = mha::launch_sdpa(a, r, dtype, mask_kind == MHA_MASK_CAUSAL, (int)d, scale, st);
   }
   // (3) out = concat · Wo
   if (e == hipSuccess) {

@@ -216,12 +216,8 @@ hipError_t launch_dt(const SdpaArgs& a, int d, hipStream_t st) {
 
 }  // namespace
 
-bool sdpa_decode_applies(const SdpaArgs& a, int dtype, int causal, int d) {
-  return (dtype == DT_BF16 || dtype == DT_F16) && !causal && !a.window && a.n_q == 1 &&
-         (d == 64 || d == 128) && a.n_k >= 512;
-}
-
 hipError_t launch_sdpa_decode(const SdpaArgs& a, int dtype, int d, hipStream_t st) {
+  if (a.n_q != 1 || (d != 64 && d != 128)) return hipErrorInvalidValue;
   return dtype == DT_BF16 ? launch_dt<DT_BF16>(a, d, st) : launch_dt<DT_F16>(a, d, st);
 }
 

@@ -53,8 +53,10 @@
 // reads of a phase hit all 64 banks once.  The buffer range ends at the valid key
 // length, so rows past it read as 0 without per-lane branches: whatever
 // the memory there holds -- NaN included -- has no effect, matching the
-// reading that a masked key has weight exactly 0; masked causal and window
-// tiles clear the V values of keys no row of the wave sees.  Causal tiles
+// reading that a masked key has weight exactly 0.  Masked causal and window
+// tiles check their value fragments for NaN/inf, whose product with a zero
+// weight would still be NaN, and if there is one, clear them for the matrix
+// product and add them back to the rows that see their keys.  Causal tiles
 // entirely above the diagonal are never loaded, tiles a whole wave cannot
 // see are skipped by that wave, and only the diagonal, window-edge and
 // key-length boundary tiles evaluate the per-element mask.
@@ -181,7 +183,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   // memory by one XCD (round-robin heads measured as fast but re-read them:
   // 79 MB against 67 MB per launch); otherwise consecutive workgroups are
   // different heads at the same rows.
-  const uint32_t t = PAIRS ? blockIdx.x : xcd_remap(blockIdx.x, total);
+  const uint32_t hw = p.reverse ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
+  const uint32_t t = PAIRS ? hw : xcd_remap(hw, total);
   const uint32_t nbh = (uint32_t)p.B * p.H;
   const bool xcd_heads = PAIRS && nbh % 8 == 0;
   const uint32_t hpx = nbh / 8, xk = t / 8;
@@ -247,18 +250,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(vaddr >> 32) & 0xffffu),
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((int64_t)n_eff * p.v_sr * 2)),
                      0x00020000u};
-
-  // Keys that some existing row of this wave can see (causal, window).  In
-  // masked tiles the V values of the other keys are zeroed before P·V: their
-  // weights are 0 already, but 0·NaN would still let a NaN value row through.
-  int vlo = 0, vhi = n_eff;
-  if (CAUSAL) {
-    const int top = row0[1] < p.n_q ? row0[1] : row0[0];  // the wave's highest existing block
-    vhi = min(n_eff, min(top + 31, p.n_q - 1) + 1);
-  } else if (WINDOW) {
-    vlo = max(0, row0[0] - p.win_left);
-    vhi = min(n_eff, min(row0[0] + 63, p.n_q - 1) + p.win_right + 1);
-  }
 
   // ---- Q fragments (B operand), resident for the whole kernel
   u32x4 qf[QB][NST];
@@ -418,25 +409,64 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   asm volatile("s_barrier" ::: "memory");
 
-  // Zero the Vᵀ fragment values of keys outside [vlo, vhi).  Element j of a
-  // fragment holds key 4·hi + (j & 3) + 8·(j >> 2) of its 16-key step; dword
-  // w holds elements 2w (low half) and 2w + 1.
-  auto zero_unseen_v = [&](u32x4 (&vf)[2][2][NDB], int kbase) __attribute__((always_inline)) {
-    if (kbase >= vlo && kbase + BN <= vhi) return;  // (wave-uniform) every key of the tile seen
+  // Non-finite values in masked causal and window tiles.  A masked score has
+  // weight exactly 0, but inside the matrix product 0·NaN and 0·inf are NaN,
+  // so a NaN or ±inf value row would reach every row of the 32-row block
+  // that loads it, also rows that do not see its key.  The masked tiles
+  // therefore check their Vᵀ fragments (wave-uniform; no such value: the
+  // common path, unchanged); when one is there, the fragments go into P·V
+  // with their non-finite elements cleared, and afterwards each row adds
+  // those elements of the keys it does see (a visible key's weight is
+  // positive, so p·x and x are the same NaN or infinity).
+  auto v_has_nonfinite = [&](const u32x4 (&vf)[2][2][NDB]) __attribute__((always_inline)) {
+    u16x2 acc = {0, 0};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const int k0 = kbase + kb * 32 + t2 * 16 + 4 * hi;
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int ka = k0 + ((2 * w) & 3) + 8 * ((2 * w) >> 2);
-          const uint32_t keep = (ka >= vlo && ka < vhi ? 0x0000ffffu : 0u) |
-                                (ka + 1 >= vlo && ka + 1 < vhi ? 0xffff0000u : 0u);
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) vf[kb][t2][db][w] &= keep;
+          for (int w = 0; w < 4; ++w) acc = magnitude_max(acc, vf[kb][t2][db][w]);
+    constexpr unsigned short lim = nonfinite_from<DT>();
+    return __builtin_amdgcn_ballot_w64(acc[0] >= lim || acc[1] >= lim) != 0;
+  };
+  auto v_clear_nonfinite = [&](u32x4 (&vf)[2][2][NDB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) vf[kb][t2][db][w] = zero_nonfinite<DT>(vf[kb][t2][db][w]);
+  };
+  // O of query block qi += the non-finite elements of the values of the keys
+  // of LDS stage buf (keys kbase ..) that the lane's row sees.  This lane's
+  // accumulator element i of 32-row block db holds column
+  // d = db·32 + 8·(i / 4) + 4·hi + i % 4: four consecutive columns per group
+  // of four, read from the value row as one 8-byte word.
+  auto add_nonfinite_v = [&](int qi, int buf, int kbase) __attribute__((always_inline)) {
+    const int row = row0[qi] + l32;
+    for (int k = 0; k < BN; ++k) {
+      const int key = kbase + k;
+      bool vis = key < n_eff;
+      if constexpr (CAUSAL) vis = vis && key <= row;
+      if constexpr (WINDOW) vis = vis && key >= row - p.win_left && key <= row + p.win_right;
+      if (!vis) continue;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * hi;
+          if (d >= D) continue;  // D = 16: the padding rows of Oᵀ
+          const u32x2 w = *(const u32x2*)&Vs[kvw][buf][k * D + (((d >> 3) ^ vswz<D>(k)) * 8) + (d & 7)];
+          const f32x4 x = unpack4<DT>(w);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!__builtin_isfinite(x[e])) o[qi][db][4 * g + e] += x[e];
         }
-      }
+    }
   };
 
   // weights of key block kb of query block qi against the current reference
@@ -571,9 +601,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
           vf[kb][t2][db] = vfrag(buf, kb, t2, db);
-    if constexpr (MASKED && (CAUSAL || WINDOW)) zero_unseen_v(vf, kbase);
     settle(masked, 0, buf, kbase, p0, rs0);
     mid();
+    // (the check right before the products: earlier, the fragments would be
+    // live across the exact path of `settle`)
+    constexpr bool CHECK_V = MASKED && (CAUSAL || WINDOW);
+    bool vbad = false;
+    if constexpr (CHECK_V) {
+      vbad = v_has_nonfinite(vf);
+      if (vbad) v_clear_nonfinite(vf);
+    }
 
 
 #pragma unroll
@@ -585,6 +622,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
           const u32x4 bv = {p0[kb][4 * t2], p0[kb][4 * t2 + 1], p0[kb][4 * t2 + 2], p0[kb][4 * t2 + 3]};
           o[0][db] = mfma_32x32x16<DT>(vf[kb][t2][db], bv, o[0][db]);
         }
+    if constexpr (CHECK_V)
+      if (vbad) add_nonfinite_v(0, buf, kbase);
     if constexpr (MASKED) {
       apply_mask(1, kbase, 0, s1[0]);
       apply_mask(1, kbase, 1, s1[1]);
@@ -606,6 +645,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
           const u32x4 bv = {p1[kb][4 * t2], p1[kb][4 * t2 + 1], p1[kb][4 * t2 + 2], p1[kb][4 * t2 + 3]};
           o[1][db] = mfma_32x32x16<DT>(vf[kb][t2][db], bv, o[1][db]);
         }
+    if constexpr (CHECK_V)
+      if (vbad) add_nonfinite_v(1, buf, kbase);
   };
 
   // One 64-key tile for block 1 only (causal: block 0 has no visible key
@@ -624,7 +665,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
           vf[kb][t2][db] = vfrag(buf, kb, t2, db);
-    if constexpr (MASKED && (CAUSAL || WINDOW)) zero_unseen_v(vf, kbase);
     if constexpr (MASKED) {
       apply_mask(1, kbase, 0, s1[0]);
       apply_mask(1, kbase, 1, s1[1]);
@@ -632,6 +672,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
     uint32_t p1[2][8];
     const float rs1 = weights(1, 0, s1[0], p1[0]) + weights(1, 1, s1[1], p1[1]);
     settle(masked, 1, buf, kbase, p1, rs1);
+    constexpr bool CHECK_V = MASKED && (CAUSAL || WINDOW);
+    bool vbad = false;
+    if constexpr (CHECK_V) {
+      vbad = v_has_nonfinite(vf);
+      if (vbad) v_clear_nonfinite(vf);
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -641,6 +687,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
           const u32x4 bv = {p1[kb][4 * t2], p1[kb][4 * t2 + 1], p1[kb][4 * t2 + 2], p1[kb][4 * t2 + 3]};
           o[1][db] = mfma_32x32x16<DT>(vf[kb][t2][db], bv, o[1][db]);
         }
+    if constexpr (CHECK_V)
+      if (vbad) add_nonfinite_v(1, buf, kbase);
   };
 
   // Two consecutive 64-key tiles (LDS buffers bufA and bufA + 1) for block 1
@@ -697,9 +745,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
           vf[kb][t2][db] = vfrag(bufA, kb, t2, db);
-    if constexpr (MASKED) zero_unseen_v(vf, kbaseA);
     settle(masked, 1, bufA, kbaseA, pa, rsa);
     mid();
+    constexpr bool CHECK_V = MASKED && CAUSAL;
+    bool vbad = false;
+    if constexpr (CHECK_V) {
+      vbad = v_has_nonfinite(vf);
+      if (vbad) v_clear_nonfinite(vf);
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -709,6 +762,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
           const u32x4 bv = {pa[kb][4 * t2], pa[kb][4 * t2 + 1], pa[kb][4 * t2 + 2], pa[kb][4 * t2 + 3]};
           o[1][db] = mfma_32x32x16<DT>(vf[kb][t2][db], bv, o[1][db]);
         }
+    if constexpr (CHECK_V)
+      if (vbad) add_nonfinite_v(1, bufA, kbaseA);
     if constexpr (MASKED) {
       apply_mask(1, kbaseB, 0, sb[0]);
       apply_mask(1, kbaseB, 1, sb[1]);
@@ -726,8 +781,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
           vf[kb][t2][db] = vfrag(bufB, kb, t2, db);
-    if constexpr (MASKED) zero_unseen_v(vf, kbaseB);
     settle(masked, 1, bufB, kbaseB, pb, rsb);
+    if constexpr (CHECK_V) {
+      vbad = v_has_nonfinite(vf);
+      if (vbad) v_clear_nonfinite(vf);
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -737,6 +795,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
           const u32x4 bv = {pb[kb][4 * t2], pb[kb][4 * t2 + 1], pb[kb][4 * t2 + 2], pb[kb][4 * t2 + 3]};
           o[1][db] = mfma_32x32x16<DT>(vf[kb][t2][db], bv, o[1][db]);
         }
+    if constexpr (CHECK_V)
+      if (vbad) add_nonfinite_v(1, bufB, kbaseB);
   };
 
   // One step of the pair layout: start the loads of the next pair (tiles
@@ -958,15 +1018,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
         }
     }
   }
-}
-
-// Workgroup size (waves of 64 query rows): 4 waves when that still gives at
-// least two workgroups per CU, else 2 (less idle padding on short
-// sequences); one wave when a head has no more than 64 query rows.  The
-// same for both masks (causal waves carry equal work by construction).
-int waves_per_wg(int64_t n_q, int64_t heads, bool /*causal*/) {
-  if (n_q <= 64) return 1;
-  return ((n_q + 255) / 256) * heads >= 512 ? 4 : 2;
 }
 
 }  // namespace

@@ -19,7 +19,9 @@
 // by key bits as in the d = 128 layout, so the fragment reads spread over
 // all banks.  Causal tiles past the block's diagonal are not computed and
 // rows past the key length read as zero; only the tiles that hold a masked
-// key for some row of the block evaluate the per-element mask.  The softmax
+// key for some row of the block evaluate the per-element mask (and check
+// their values for NaN/inf, which a zero weight would not cancel inside
+// the matrix product).  The softmax
 // has no per-tile max, as in the d <= 128 kernel: a tile's weights are
 // formed against the row's current reference value and accepted while each
 // lane's partial row sum stays <= 2^8; otherwise (and on the first tile)
@@ -104,9 +106,8 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
   float m = -INFINITY, l = 0.f, mc = 0.f;
   const float c = p.c;
   // first key masked for some row of the block (the block's first row sees
-  // keys up to itself) and first key no row of the block sees (causal)
+  // keys up to itself)
   const int mask_from = CAUSAL ? min(n_eff, row0 + 1) : n_eff;
-  const int vhi = min(n_eff, min(row0 + 31, p.n_q - 1) + 1);
   const int sx_sw = (lane >> 2) & 3;
 
   // ---- staging: a tile is BN rows of D/8 16-byte chunks, chunk c of key k
@@ -239,28 +240,66 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
     }
     l += rs;
   };
-  // this wave's columns of Oᵀ += Vᵀ·Pᵀ for the values in LDS (keys whose
-  // weight is 0 but whose value row lies past the causal diagonal of every
-  // row: cleared)
+  // this wave's columns of Oᵀ += Vᵀ·Pᵀ for the values in LDS.  In a masked
+  // causal tile a NaN or ±inf value row would reach, through 0·x in the
+  // matrix product, the rows of the block that do not see its key; those
+  // tiles check the fragments (wave-uniform), and when such a value is
+  // there they clear it for the product and add it afterwards to the rows
+  // that see the key (a visible key's weight is positive).
+  auto add_nonfinite_v = [&](int j) __attribute__((always_inline)) {
+    const int row = row0 + l32;
+    for (int k = 0; k < BN; ++k) {
+      const int key = j * BN + k;
+      if (!(key < n_eff && key <= row)) continue;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = wave * DS + db * 32 + 8 * g + 4 * hi;
+          const u32x2 w = *(const u32x2*)&Vs[k * D + (((d >> 3) ^ (4 * (k & 3))) * 8) + (d & 7)];
+          const f32x4 x = unpack4<DT>(w);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!__builtin_isfinite(x[e])) o[db][4 * g + e] += x[e];
+        }
+    }
+  };
   auto pv = [&](int j, const uint32_t (&pw)[8]) __attribute__((always_inline)) {
+    if (CAUSAL && j * BN + BN > mask_from) {
+      u32x4 vf[2][NDB];
+      u16x2 acc = {0, 0};
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          vf[t2][db] = vfrag(t2, db);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc = magnitude_max(acc, vf[t2][db][w]);
+        }
+      constexpr unsigned short lim = nonfinite_from<DT>();
+      const bool vbad = __builtin_amdgcn_ballot_w64(acc[0] >= lim || acc[1] >= lim) != 0;
+      if (vbad) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) vf[t2][db][w] = zero_nonfinite<DT>(vf[t2][db][w]);
+      }
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const u32x4 bv = {pw[4 * t2], pw[4 * t2 + 1], pw[4 * t2 + 2], pw[4 * t2 + 3]};
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = mfma_32x32x16<DT>(vf[t2][db], bv, o[db]);
+      }
+      if (vbad) add_nonfinite_v(j);
+      return;
+    }
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const u32x4 bv = {pw[4 * t2], pw[4 * t2 + 1], pw[4 * t2 + 2], pw[4 * t2 + 3]};
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        u32x4 vf = vfrag(t2, db);
-        if (CAUSAL && j * BN + BN > vhi) {
-          // keys past the block's last row are seen by no row of the block
-          const int k0 = j * BN + t2 * 16 + 4 * hi;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int ka = k0 + ((2 * w) & 3) + 8 * ((2 * w) >> 2);
-            const uint32_t keep = (ka < vhi ? 0x0000ffffu : 0u) | (ka + 1 < vhi ? 0xffff0000u : 0u);
-            vf[w] &= keep;
-          }
-        }
-        o[db] = mfma_32x32x16<DT>(vf, bv, o[db]);
-      }
+      for (int db = 0; db < NDB; ++db) o[db] = mfma_32x32x16<DT>(vfrag(t2, db), bv, o[db]);
     }
   };
 

@@ -25,9 +25,26 @@ MHA_ERR_ALIAS = -6
 MHA_ERR_HIP = -7
 
 # every symbol include/mha.h declares
-EXPORTS = ("mha_sdpa", "mha_sdpa_window", "mha_forward", "mha_forward_workspace_size", "mha_add_norm",
+EXPORTS = ("mha_sdpa", "mha_sdpa_strided", "mha_sdpa_window", "mha_sdpa_window_strided",
+           "mha_sdpa_route", "mha_forward", "mha_forward_workspace_size", "mha_add_norm",
            "mha_forward_add_norm", "mha_forward_add_norm_workspace_size", "mha_status_string",
            "mha_last_error", "mha_version")
+
+# mha_route.kernel values
+KERNELS = {0: "f32", 1: "blocks", 2: "pairs", 3: "split", 4: "decode", 5: "window", 6: "wide"}
+
+
+class SdpaStrides(ctypes.Structure):
+    """mha_sdpa_strides: [batch, head, row] element strides of Q, K, V, O."""
+    _fields_ = [("q", ctypes.c_int64 * 3), ("k", ctypes.c_int64 * 3), ("v", ctypes.c_int64 * 3),
+                ("o", ctypes.c_int64 * 3)]
+
+
+class Route(ctypes.Structure):
+    """mha_route."""
+    _fields_ = [("kernel", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("rows_per_workgroup", ctypes.c_int32), ("mask_kind", ctypes.c_int32),
+                ("workgroups", ctypes.c_int64)]
 
 _lib = None
 
@@ -53,6 +70,16 @@ def lib():
     L.mha_sdpa_window.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, f32, i64, i64,
                                   vp, vp]
     L.mha_sdpa_window.restype = ctypes.c_int
+    sp = ctypes.POINTER(SdpaStrides)
+    L.mha_sdpa_strided.argtypes = [vp, vp, vp, vp, sp, i32, i64, i64, i64, i64, i64, i64, f32, i32,
+                                   vp, vp]
+    L.mha_sdpa_strided.restype = ctypes.c_int
+    L.mha_sdpa_window_strided.argtypes = [vp, vp, vp, vp, sp, i32, i64, i64, i64, i64, i64, i64, f32,
+                                          i64, i64, vp, vp]
+    L.mha_sdpa_window_strided.restype = ctypes.c_int
+    L.mha_sdpa_route.argtypes = [i32, i64, i64, i64, i64, i64, i64, i32, i32, i64, i64,
+                                 ctypes.POINTER(Route)]
+    L.mha_sdpa_route.restype = ctypes.c_int
     L.mha_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32, i32, vp,
                               vp, ctypes.c_size_t, vp]
     L.mha_forward.restype = ctypes.c_int
@@ -125,6 +152,11 @@ def _contig(t, name):
     return t
 
 
+def _scale(scale):
+    """None -> NaN: the library then uses 1/sqrt(d_k)."""
+    return float("nan") if scale is None else float(scale)
+
+
 def _lens(t, B, name):
     if t is None:
         return None
@@ -144,14 +176,12 @@ def sdpa(Q, K, V, scale=None, mask="none", seq_lens=None, out=None, stream=None)
             raise ValueError(f"{n} must be 4-d [B, h, n, d]")
     B, h, n_q, d_k = Q.shape
     n_k, d_v = K.shape[2], V.shape[3]
-    if scale is None:
-        scale = 1.0 / float(d_k) ** 0.5
     if out is None:
         out = torch.empty((B, h, n_q, d_v), dtype=Q.dtype, device=Q.device)
     _contig(out, "out")
     lens = _lens(seq_lens, B, "seq_lens")
     _check(lib().mha_sdpa(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), dtype_code(Q), B, h, n_q, n_k,
-                          d_k, d_v, float(scale), _mask_code(mask), _ptr(lens), _stream(stream)))
+                          d_k, d_v, _scale(scale), _mask_code(mask), _ptr(lens), _stream(stream)))
     return out
 
 
@@ -165,16 +195,80 @@ def sdpa_window(Q, K, V, left, right, scale=None, seq_lens=None, out=None, strea
             raise ValueError(f"{n} must be 4-d [B, h, n, d]")
     B, h, n_q, d_k = Q.shape
     n_k, d_v = K.shape[2], V.shape[3]
-    if scale is None:
-        scale = 1.0 / float(d_k) ** 0.5
     if out is None:
         out = torch.empty((B, h, n_q, d_v), dtype=Q.dtype, device=Q.device)
     _contig(out, "out")
     lens = _lens(seq_lens, B, "seq_lens")
     _check(lib().mha_sdpa_window(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), dtype_code(Q), B, h, n_q,
-                                 n_k, d_k, d_v, float(scale), int(left), int(right), _ptr(lens),
+                                 n_k, d_k, d_v, _scale(scale), int(left), int(right), _ptr(lens),
                                  _stream(stream)))
     return out
+
+
+def _bhnd(t, name):
+    """(shape, [batch, head, row] strides) of a [B, h, n, d] tensor view whose
+    last axis is contiguous."""
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-d [B, h, n, d]")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError(f"{name}: the last axis must be contiguous")
+    # (a dimension of size 1 is never stepped along: its stride is passed as 0)
+    return tuple(t.shape), tuple(0 if t.shape[i] == 1 else t.stride(i) for i in range(3))
+
+
+def _strides(Q, K, V, O):
+    st = SdpaStrides()
+    for f, t, n in (("q", Q, "Q"), ("k", K, "K"), ("v", V, "V"), ("o", O, "out")):
+        getattr(st, f)[:] = _bhnd(t, n)[1]
+    return st
+
+
+def sdpa_strided(Q, K, V, scale=None, mask="none", seq_lens=None, out=None, stream=None):
+    """mha_sdpa_strided: as sdpa(), for [B, h, n, d] views with any strides
+    (last axis contiguous), e.g. ``x.view(B, n, h, d).transpose(1, 2)``.
+    ``out`` may be a strided view too (allocated contiguous if None)."""
+    import torch
+    (B, h, n_q, d_k), _ = _bhnd(Q, "Q")
+    (_, _, n_k, _), _ = _bhnd(K, "K")
+    d_v = V.shape[3]
+    if out is None:
+        out = torch.empty((B, h, n_q, d_v), dtype=Q.dtype, device=Q.device)
+    lens = _lens(seq_lens, B, "seq_lens")
+    st = _strides(Q, K, V, out)
+    _check(lib().mha_sdpa_strided(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), ctypes.byref(st),
+                                  dtype_code(Q), B, h, n_q, n_k, d_k, d_v, _scale(scale),
+                                  _mask_code(mask), _ptr(lens), _stream(stream)))
+    return out
+
+
+def sdpa_window_strided(Q, K, V, left, right, scale=None, seq_lens=None, out=None, stream=None):
+    """mha_sdpa_window_strided: sdpa_window() on strided views."""
+    import torch
+    (B, h, n_q, d_k), _ = _bhnd(Q, "Q")
+    (_, _, n_k, _), _ = _bhnd(K, "K")
+    d_v = V.shape[3]
+    if out is None:
+        out = torch.empty((B, h, n_q, d_v), dtype=Q.dtype, device=Q.device)
+    lens = _lens(seq_lens, B, "seq_lens")
+    st = _strides(Q, K, V, out)
+    _check(lib().mha_sdpa_window_strided(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), ctypes.byref(st),
+                                         dtype_code(Q), B, h, n_q, n_k, d_k, d_v, _scale(scale),
+                                         int(left), int(right), _ptr(lens), _stream(stream)))
+    return out
+
+
+def sdpa_route(dtype, B, h, n_q, n_k, d_k, mask="none", window=None, d_v=None):
+    """mha_sdpa_route: the kernel mha_sdpa (or, with ``window`` = (left,
+    right), mha_sdpa_window) runs for these sizes.  ``dtype`` is an MHA_*
+    code.  Returns a dict; needs no device."""
+    r = Route()
+    left, right = (0, 0) if window is None else window
+    _check(lib().mha_sdpa_route(int(dtype), B, h, n_q, n_k, d_k, d_k if d_v is None else d_v,
+                                _mask_code(mask), 0 if window is None else 1, int(left), int(right),
+                                ctypes.byref(r)))
+    return {"kernel": KERNELS.get(r.kernel, r.kernel), "waves": r.waves,
+            "rows_per_workgroup": r.rows_per_workgroup, "mask_kind": r.mask_kind,
+            "workgroups": r.workgroups}
 
 
 def workspace_size(B, n_q, n_k, d_model, h, dtype):
