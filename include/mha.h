@@ -28,8 +28,10 @@
  *   (round to nearest even).
  * - B = 0, h = 0 or n_q = 0 is a successful no-op.  n_k = 0 or a key length
  *   of 0 gives all-zero output rows (a row with nothing visible).
- * - The library holds no mutable global state; concurrent calls on
- *   different streams are safe as long as their buffers do not overlap.
+ * - The library's only mutable state is the device address of the scratch
+ *   array of mha_forward_noalloc (looked up once per device, under a lock);
+ *   concurrent calls on different streams are safe as long as their buffers
+ *   do not overlap (mha_forward_noalloc: see there).
  * - Setting the environment variable MHA_TRACE=1 logs every dispatch
  *   (kernel, grid, algorithmic bytes and flops) to stderr.
  *   MHA_GRID_ORDER=reverse launches the attention workgroups in the opposite
@@ -205,6 +207,27 @@ int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* W
 /* Workspace bytes mha_forward needs for these sizes (0 for invalid sizes). */
 size_t mha_forward_workspace_size(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model,
                                   int32_t h, int32_t dtype);
+
+/*
+ * mha_forward for callers that cannot allocate: code being captured into a
+ * HIP graph, tight serving loops, harnesses that forbid allocation.  Same
+ * computation, arguments (no workspace) and errors as mha_forward; it calls
+ * no allocating routine.  Its workspace is a scratch array inside the
+ * library, MHA_NOALLOC_SCRATCH_BYTES (32 MiB) on every GPU the library runs
+ * on, held until the process ends: sizes whose mha_forward_workspace_size()
+ * exceeds it return MHA_ERR_WORKSPACE (the big-model cross-attention
+ * sub-layer, B 8, n_q 384, n_k 512, d_model 1024, needs 29.4 MB).  Every
+ * call on one GPU shares that GPU's array (each call fully writes what it
+ * reads from it, so no clearing is needed): calls that overlap in time on one
+ * GPU -- on different streams, or from different threads -- race and must
+ * be serialised by the caller.  The array's device address is looked up on
+ * the first call on each device (a HIP runtime query, not an allocation).
+ */
+#define MHA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int mha_forward_noalloc(const void* x_q, const void* x_kv, const void* Wq, const void* Wk,
+                        const void* Wv, const void* Wo, void* out, int32_t dtype, int64_t B,
+                        int64_t n_q, int64_t n_k, int64_t d_model, int32_t h, int32_t mask_kind,
+                        const int32_t* kv_lens, void* stream);
 
 /*
  * Residual connection and layer normalisation ("Add & Norm"), [N] the

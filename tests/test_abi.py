@@ -247,6 +247,37 @@ def test_forward_rejects(kw, code):
     assert _fwd(**kw) == code
 
 
+def _fna(B=2, n_q=8, n_k=8, d_model=128, h=2, dtype=M.MHA_BF16, x_kv=None, mask=M.MHA_MASK_NONE,
+         out=0x500000):
+    return M.lib().mha_forward_noalloc(0x1000, x_kv, 0x100000, 0x200000, 0x300000, 0x400000, out,
+                                       dtype, B, n_q, n_k, d_model, h, mask, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=8, n_q=4096, n_k=4096, d_model=1024, h=16), M.MHA_ERR_WORKSPACE),   # 268 MB > 32 MiB
+    (dict(dtype=M.MHA_F32), M.MHA_ERR_UNSUPPORTED),
+    (dict(d_model=129), M.MHA_ERR_SHAPE),
+    (dict(n_k=9), M.MHA_ERR_SHAPE),
+    (dict(mask=7), M.MHA_ERR_INVALID_ARG),
+    (dict(dtype=9), M.MHA_ERR_DTYPE),
+])
+def test_forward_noalloc_rejects(kw, code):
+    """Oversized problems are refused before anything touches a device; bad
+    arguments give mha_forward's errors."""
+    assert _fna(**kw) == code
+    assert M.last_error().startswith("mha_forward_noalloc")
+
+
+def test_forward_noalloc_limit():
+    """The largest workspace the scratch takes: the big-model cross-attention
+    sub-layer fits, twice its batch does not."""
+    L = M.lib()
+    assert L.mha_forward_workspace_size(8, 384, 512, 1024, 16, M.MHA_BF16) <= M.NOALLOC_SCRATCH_BYTES
+    assert L.mha_forward_workspace_size(16, 384, 512, 1024, 16, M.MHA_BF16) > M.NOALLOC_SCRATCH_BYTES
+    assert _fna(B=16, n_q=384, n_k=512, d_model=1024, h=16, x_kv=0x900000) == M.MHA_ERR_WORKSPACE
+    assert _fna(B=0) == M.MHA_OK
+
+
 def test_forward_zero_sizes_are_noops():
     assert _fwd(B=0) == M.MHA_OK
     assert _fwd(n_q=0, n_k=0) == M.MHA_OK

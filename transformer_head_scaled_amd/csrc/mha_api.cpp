@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <utility>
 
 #include "kernels.h"
@@ -90,6 +91,34 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(MHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// The workspace of mha_forward_noalloc: a device array of this library, one
+// copy on every GPU that loads it, held until the process ends.  Its name in
+// host code is only a stand-in for the symbol; the device address comes from
+// hipGetSymbolAddress, once per device, and is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[MHA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// this device's address of `scratch` (looked up on the first call on it)
+int scratch_on_current_device(const char* fn, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(MHA_ERR_HIP, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (!p) return fail(MHA_ERR_HIP, "%s: no device address for the scratch array", fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MHA_OK;
 }
 
 }  // namespace
@@ -360,7 +389,7 @@ static int forward_impl(const char* fn, const void* x_q, const void* x_kv, const
                         const void* an_beta, float an_eps, void* out, int32_t dtype, int64_t B,
                         int64_t n_q, int64_t n_k, int64_t d_model, int32_t h, int32_t mask_kind,
                         const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        void* stream, bool noalloc = false) {
   const bool an = an_gamma != nullptr || an_beta != nullptr;
   if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16)
     return fail(MHA_ERR_DTYPE, "%s: dtype %d", fn, (int)dtype);
@@ -412,6 +441,9 @@ static int forward_impl(const char* fn, const void* x_q, const void* x_kv, const
   if (workspace && workspace_bytes < ws_need)
     return fail(MHA_ERR_WORKSPACE, "%s: workspace %zu bytes, needs %zu", fn, workspace_bytes,
                 ws_need);
+  if (noalloc && ws_need > (size_t)MHA_NOALLOC_SCRATCH_BYTES)
+    return fail(MHA_ERR_WORKSPACE, "%s: these sizes need %zu bytes of scratch, above its %zu", fn,
+                ws_need, (size_t)MHA_NOALLOC_SCRATCH_BYTES);
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return fail(MHA_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
   const size_t wbytes = (size_t)(d_model * d_model) * es;
@@ -429,6 +461,14 @@ static int forward_impl(const char* fn, const void* x_q, const void* x_kv, const
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   bool owned = false;
+  if (noalloc) {  // every argument is valid: the scratch array of this device
+    void* p = nullptr;
+    const int rc = scratch_on_current_device(fn, &p);
+    if (rc != MHA_OK) return rc;
+    ws = (char*)p;
+    if (overlap(ro, range_of(ws, ws_need)))
+      return fail(MHA_ERR_ALIAS, "%s: out overlaps the library's scratch array", fn);
+  }
   if (!ws) {
     const hipError_t e = hipMallocAsync((void**)&ws, ws_need, st);
     if (e != hipSuccess) return hip_fail(e, "workspace allocation");
@@ -521,6 +561,15 @@ int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* W
   return forward_impl("mha_forward", x_q, x_kv, Wq, Wk, Wv, Wo, nullptr, nullptr, 0.f, out, dtype,
                       B, n_q, n_k, d_model, h, mask_kind, kv_lens, workspace, workspace_bytes,
                       stream);
+}
+
+int mha_forward_noalloc(const void* x_q, const void* x_kv, const void* Wq, const void* Wk,
+                        const void* Wv, const void* Wo, void* out, int32_t dtype, int64_t B,
+                        int64_t n_q, int64_t n_k, int64_t d_model, int32_t h, int32_t mask_kind,
+                        const int32_t* kv_lens, void* stream) {
+  return forward_impl("mha_forward_noalloc", x_q, x_kv, Wq, Wk, Wv, Wo, nullptr, nullptr, 0.f, out,
+                      dtype, B, n_q, n_k, d_model, h, mask_kind, kv_lens, nullptr, 0, stream,
+                      /*noalloc=*/true);
 }
 
 int mha_forward_add_norm(const void* x_q, const void* x_kv, const void* Wq, const void* Wk,

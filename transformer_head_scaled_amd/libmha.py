@@ -23,10 +23,12 @@ MHA_ERR_UNSUPPORTED = -4
 MHA_ERR_WORKSPACE = -5
 MHA_ERR_ALIAS = -6
 MHA_ERR_HIP = -7
+NOALLOC_SCRATCH_BYTES = 32 << 20   # MHA_NOALLOC_SCRATCH_BYTES
 
 # every symbol include/mha.h declares
 EXPORTS = ("mha_sdpa", "mha_sdpa_strided", "mha_sdpa_window", "mha_sdpa_window_strided",
-           "mha_sdpa_route", "mha_forward", "mha_forward_workspace_size", "mha_add_norm",
+           "mha_sdpa_route", "mha_forward", "mha_forward_workspace_size", "mha_forward_noalloc",
+           "mha_add_norm",
            "mha_forward_add_norm", "mha_forward_add_norm_workspace_size", "mha_status_string",
            "mha_last_error", "mha_version")
 
@@ -83,6 +85,9 @@ def lib():
     L.mha_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32, i32, vp,
                               vp, ctypes.c_size_t, vp]
     L.mha_forward.restype = ctypes.c_int
+    L.mha_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32,
+                                      i32, vp, vp]
+    L.mha_forward_noalloc.restype = ctypes.c_int
     L.mha_forward_workspace_size.argtypes = [i64, i64, i64, i64, i32, i32]
     L.mha_forward_workspace_size.restype = ctypes.c_size_t
     L.mha_add_norm.argtypes = [vp, vp, vp, vp, f32, vp, i32, i64, i64, vp]
@@ -298,6 +303,29 @@ def forward(x_q, Wq, Wk, Wv, Wo, h, x_kv=None, mask="none", kv_lens=None, out=No
                              _ptr(out), dtype_code(x_q), B, n_q, n_k, d_model, int(h),
                              _mask_code(mask), _ptr(lens), _ptr(workspace), ws_bytes,
                              _stream(stream)))
+    return out
+
+
+def forward_noalloc(x_q, Wq, Wk, Wv, Wo, h, x_kv=None, mask="none", kv_lens=None, out=None,
+                    stream=None):
+    """mha_forward_noalloc: forward() with the library's own scratch array as
+    the workspace (no allocation inside the call; calls overlapping on one
+    GPU race).  ``out`` must be given by callers that cannot allocate."""
+    import torch
+    for n, t in (("x_q", x_q), ("x_kv", x_kv), ("Wq", Wq), ("Wk", Wk), ("Wv", Wv), ("Wo", Wo)):
+        _contig(t, n)
+    B, n_q, d_model = x_q.shape
+    n_k = n_q if x_kv is None else x_kv.shape[1]
+    for n, t in (("Wq", Wq), ("Wk", Wk), ("Wv", Wv), ("Wo", Wo)):
+        if tuple(t.shape) != (d_model, d_model):
+            raise ValueError(f"{n} must be [{d_model}, {d_model}]")
+    if out is None:
+        out = torch.empty((B, n_q, d_model), dtype=x_q.dtype, device=x_q.device)
+    _contig(out, "out")
+    lens = _lens(kv_lens, B, "kv_lens")
+    _check(lib().mha_forward_noalloc(_ptr(x_q), _ptr(x_kv), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wo),
+                                     _ptr(out), dtype_code(x_q), B, n_q, n_k, d_model, int(h),
+                                     _mask_code(mask), _ptr(lens), _stream(stream)))
     return out
 
 
