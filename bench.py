@@ -122,6 +122,19 @@ def other_configs(dev, stream, iters=100):
         scratch.sum()
 
     res = {}
+    # the single-head fp32 case: launch latency, neither roofline applies
+    w = synth.WORKLOADS[1]
+    ins1 = synth.sdpa_inputs(1, w["B"], w["h"], w["n_q"], w["n_k"], w["d"], dtype="f32")
+    Q1, K1, V1 = (torch.from_numpy(ins1[k][0]).to(dev) for k in "QKV")
+    O1 = torch.empty_like(Q1)
+
+    def call1():
+        libmha.sdpa(Q1, K1, V1, scale=0.125, out=O1, stream=stream)
+    for _ in range(20):
+        call1()
+    med, mn = time_calls(call1, stream, iters)
+    res[w["name"]] = {"call": "mha_sdpa f32", "us_median": round(med, 2), "us_min": round(mn, 2),
+                      "flops": sdpa_flops(1, 1, 16, 16, 64, False), "bytes": 4 * 16 * 64 * 4}
     for cfg in (2, 4):
         w = synth.WORKLOADS[cfg]
         ins, lens = synth.workload_inputs(cfg)
@@ -290,6 +303,56 @@ def head_dim_sweep(dev, stream, B=4, n=4096, iters=50, settle_s=1.0):
     return res
 
 
+def profile_workloads(dev, names, steps):
+    """Run each named workload ``steps`` times, warm, back to back (for the
+    rocprofv3 counter passes, whose per-dispatch readings then belong to one
+    workload each).  Names: nc, c (the long-sequence batch unmasked and
+    causal), cfg1, cfg2, cfg3, cfg4."""
+    import numpy as np
+    import torch
+    from transformer_head_scaled_amd import libmha, synth
+
+    def dev_t(st):
+        return torch.from_numpy(np.ascontiguousarray(st).view(np.int16)).to(dev).view(torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    done = []
+    for name in names:
+        if name in ("nc", "c", "cfg3", "cfg1"):
+            cfg = {"nc": 5, "c": 5, "cfg3": 3, "cfg1": 1}[name]
+            w = synth.WORKLOADS[cfg]
+            ins = synth.sdpa_inputs(cfg, w["B"], w["h"], w["n_q"], w["n_k"], w["d"], dtype=w["dtype"])
+            if w["dtype"] == "f32":
+                Q, K, V = (torch.from_numpy(ins[k][0]).to(dev) for k in "QKV")
+            else:
+                Q, K, V = (dev_t(ins[k][0]) for k in "QKV")
+            O = torch.empty_like(Q)
+            mask = "none" if name in ("nc", "cfg1") else "causal"
+
+            def call():
+                libmha.sdpa(Q, K, V, scale=0.125, mask=mask, out=O, stream=stream)
+        elif name in ("cfg2", "cfg4"):
+            cfg = int(name[3])
+            w = synth.WORKLOADS[cfg]
+            ins, lens = synth.workload_inputs(cfg)
+            t = {k: dev_t(v[0]) for k, v in ins.items()}
+            lens_d = None if lens is None else torch.from_numpy(lens).to(dev)
+            B, n_q, n_k, dm, h = w["B"], w["n_q"], w["n_k"], w["d_model"], w["h"]
+            ws = torch.empty(libmha.workspace_size(B, n_q, n_k, dm, h, 1), dtype=torch.uint8, device=dev)
+            out = torch.empty((B, n_q, dm), dtype=torch.bfloat16, device=dev)
+
+            def call():
+                libmha.forward(t["x_q"], t["Wq"], t["Wk"], t["Wv"], t["Wo"], h, x_kv=t.get("x_kv"),
+                               kv_lens=lens_d, out=out, workspace=ws, stream=stream)
+        else:
+            raise SystemExit(f"unknown workload {name}")
+        for _ in range(3 + steps):
+            call()
+        torch.cuda.synchronize()
+        done.append(name)
+    print(json.dumps({"profiled": done, "calls_each": 3 + steps}), flush=True)
+    return 0
+
+
 def cpu_baseline(ins, budget_s=12.0):
     """The fp64 oracle, untuned, on a bounded sample of the same workload:
     whole (batch, head) pairs, alternating unmasked and causal, until the
@@ -298,9 +361,19 @@ def cpu_baseline(ins, budget_s=12.0):
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl missing
-        cores = 1
+        blas = 1
+    host_cores = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     Q, K, V = (ins[n][1].astype(np.float64) for n in "QKV")
     B, h, n, d = Q.shape
     done, flops, t_total = [], 0.0, 0.0
@@ -315,7 +388,11 @@ def cpu_baseline(ins, budget_s=12.0):
         flops += sdpa_flops(1, 1, n, n, d, causal)
         done.append(f"({b},{i},{'causal' if causal else 'none'})")
         k += 1
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    # cores: the threads the oracle actually ran on -- numpy's BLAS threads
+    # (the matrix products), at most the host cores this process may use
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": min(blas, host_cores),
+            "kind": "oracle", "blas_threads": blas, "host_cores_available": host_cores,
+            "cpu_model": cpu_model,
             "sample": f"{len(done)} whole heads of [4,8,4096,64] (alternating unmasked/causal, "
                       f"first {done[0]} .. last {done[-1]}), {t_total:.1f} s fp64 numpy"}
 
@@ -336,6 +413,9 @@ def main():
                     help="only time the head-dimension variants (d_k 16/32/64/128) of mha_sdpa")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (for scaling HBM counters)")
+    ap.add_argument("--profile-workload", default=None,
+                    help="only run these workloads --steps times each, warm (comma-separated: nc, c, "
+                         "cfg1, cfg2, cfg3, cfg4), for the counter passes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: libmha runs on one GPU only (no multi-GPU path is built); "
@@ -356,6 +436,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
         return 0
+    if args.profile_workload:
+        return profile_workloads(dev, args.profile_workload.split(","), args.steps)
     if args.head_dims:
         out = {"head_dim_variants": head_dim_sweep(dev, torch.cuda.current_stream()),
                "dtype": "bf16", "data": "synthetic", "unit": "TFLOP/s"}
@@ -373,15 +455,9 @@ def main():
     O_c = torch.empty_like(Q)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         libmha.sdpa(Q, K, V, scale=0.125, mask="none", out=O_nc, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
         libmha.sdpa(Q, K, V, scale=0.125, mask="causal", out=O_c, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
 
     t_settle = time.perf_counter()
     while time.perf_counter() - t_settle < args.settle_seconds:
@@ -399,13 +475,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per-launch kernel durations: HIP events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for e in evs:
-        step(e)
-    torch.cuda.synchronize()
-    nc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    c_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # average launch duration of each mode's kernel: K launches back to back
+    # on the launch stream between one pair of HIP events (events around
+    # every launch would add their own ~2 µs to each)
+    def mode_ms(mask, out):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            libmha.sdpa(Q, K, V, scale=0.125, mask=mask, out=out, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+    nc_ms = mode_ms("none", O_nc)
+    c_ms = mode_ms("causal", O_c)
 
     f_nc = sdpa_flops(B, h, n, n, d, False)
     f_c = sdpa_flops(B, h, n, n, d, True)
@@ -459,7 +541,9 @@ def main():
     if not args.no_other_configs:
         res["other_configs"] = other_configs(dev, stream)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(ins, args.cpu_budget)
+        cb = cpu_baseline(ins, args.cpu_budget)
+        cb["gpu_over_cpu"] = round(value / cb["value"], 1)   # information only
+        res["cpu_baseline"] = cb
     print(json.dumps(res), flush=True)
     return 0
 

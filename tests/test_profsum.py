@@ -83,9 +83,16 @@ def test_traffic_scales_by_the_copy(tmp_path):
     write_run(str(tmp_path / "w"), [(k, 0, 1, {"WRITE_SIZE": 500.0}), (kc, 0, 1, {"WRITE_SIZE": 500.0})])
     write_run(str(tmp_path / "cf"), [(copy, 0, 1, {"FETCH_SIZE": 2.0 * cb / 1024.0})])
     write_run(str(tmp_path / "cw"), [(copy, 0, 1, {"WRITE_SIZE": cb / 1024.0})])
-    res = profsum.traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"),
-                          str(tmp_path / "cw"), str(tmp_path / "t.json"), "cmds")
+    # a second workload group, its own pair of runs
+    k3 = "void mha::(anonymous namespace)::sdpa_fwd_kernel<1, 64, true, 4, false, false, true>(mha::SdpaArgs)"
+    write_run(str(tmp_path / "f3"), [(k3, 0, 1, {"FETCH_SIZE": 64.0})])
+    write_run(str(tmp_path / "w3"), [(k3, 0, 1, {"WRITE_SIZE": 32.0})])
+    res = profsum.traffic(str(tmp_path / "cf"), str(tmp_path / "cw"), str(tmp_path / "t.json"), "cmds",
+                          {"bench": (str(tmp_path / "f"), str(tmp_path / "w")),
+                           "cfg3": (str(tmp_path / "f3"), str(tmp_path / "w3"))})
     assert res["fetch_factor"] == 0.5 and res["write_factor"] == 1.0
+    assert res["runs"]["cfg3"][k3]["bytes_per_launch"] == 64.0 * 1024 * 0.5 + 32.0 * 1024
+    assert k3 not in res["runs"]["bench"]
     assert res["noncausal_bytes_per_launch"] == 1000.0 * 1024 * 0.5 + 500.0 * 1024
     assert res["causal_bytes_per_launch"] == 3000.0 * 1024 * 0.5 + 500.0 * 1024
     assert res["kernel_source_sha256_16"] == profsum.kernel_hash()

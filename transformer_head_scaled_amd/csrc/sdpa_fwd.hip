@@ -12,12 +12,15 @@ namespace {
 // ---------------------------------------------------------------- fp32 path
 //
 // Plain fp32 attention for small problems and the 1e-5 parity case: one
-// thread per query row, K/V tiles of 32 keys broadcast from LDS, online
-// softmax.  Any head dimension in {16, 32, 64, 128}.  Inputs, weights and
-// the output accumulator are fp32; the dot products, the running max and
-// the exponent argument are formed in fp64, so the scores carry no fp32
-// summation error even when they are large (an unscaled softmax), and the
-// only fp32 roundings left are expf and the weighted sum of V.
+// thread per query row, K/V tiles of 32 keys broadcast from LDS, and the
+// online softmax taken one key at a time (the running max moves only when a
+// key beats it, and only then are O and the sum rescaled).  Any head
+// dimension in {16, 32, 64, 128}.  Inputs and the output accumulator are
+// fp32; each dot product, the running max and the exponent argument are
+// formed in fp64, so the scores carry no fp32 summation error even when they
+// are large (an unscaled softmax), and the only fp32 roundings left are expf
+// and the weighted sum of V.  The key loop is not unrolled: the query row and
+// the output row stay in registers and nothing spills.
 template <int DH>
 __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, int causal) {
   constexpr int TK = 32;
@@ -40,6 +43,13 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
     jlo = max(0, (int)blockIdx.x * 64 - p.win_left) / TK;
   }
   const int ntiles = kend > 0 ? (kend + TK - 1) / TK : 0;
+  // this row's visible keys: [lo, hi)
+  int lo = 0, hi = n_eff;
+  if (causal) hi = min(hi, row + 1);
+  if (p.window) {
+    lo = max(lo, row - p.win_left);
+    hi = min(hi, row + p.win_right + 1);
+  }
 
   float q[DH], o[DH];
 #pragma unroll
@@ -63,36 +73,27 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
       *(float4*)&Vs[e * 4] = vv;
     }
     __syncthreads();
-    double s[TK];
-    double mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < TK; ++k) {
+    // a masked key is skipped outright (not added with weight 0), so the
+    // values it holds -- NaN included -- never reach this row
+    const int k0 = max(lo - j * TK, 0), k1 = min(hi - j * TK, TK);
+#pragma unroll 1
+    for (int k = k0; k < k1; ++k) {
       double acc = 0.0;
 #pragma unroll
       for (int d = 0; d < DH; ++d) acc = __builtin_fma((double)q[d], (double)Ks[k * DH + d], acc);
-      const int key = j * TK + k;
-      const bool vis = key < n_eff && (!causal || key <= row) &&
-                       (!p.window || (key >= row - p.win_left && key <= row + p.win_right));
-      s[k] = vis ? acc * (double)scale : -INFINITY;
-      mx = fmax(mx, s[k]);
-    }
-    const double m_new = fmax(m, mx);
-    const float alpha = (m == -INFINITY) ? 0.f : expf((float)(m - m_new));
-    const double mu = m_new == -INFINITY ? 0.0 : m_new;
-    l *= alpha;
+      const double sc = acc * (double)scale;
+      if (sc > m) {  // a new running max: rescale what has been summed
+        const float alpha = (m == -INFINITY) ? 0.f : expf((float)(m - sc));
+        l *= alpha;
 #pragma unroll
-    for (int d = 0; d < DH; ++d) o[d] *= alpha;
-#pragma unroll
-    for (int k = 0; k < TK; ++k) {
-      // a masked key is skipped outright (not added with weight 0), so the
-      // values it holds -- NaN included -- never reach this row
-      if (s[k] == -INFINITY) continue;
-      const float e = expf((float)(s[k] - mu));
+        for (int d = 0; d < DH; ++d) o[d] *= alpha;
+        m = sc;
+      }
+      const float e = expf((float)(sc - m));
       l += e;
 #pragma unroll
       for (int d = 0; d < DH; ++d) o[d] = __builtin_fmaf(e, Vs[k * DH + d], o[d]);
     }
-    m = m_new;
   }
   if (row < p.n_q) {
     const float inv = l > 0.f ? 1.f / l : 0.f;

@@ -1,17 +1,19 @@
 """Summarise rocprofv3 CSV output into the short text/JSON kept under profiles/.
 
     python -m transformer_head_scaled_amd.profsum stats  <kernel_stats.csv> <out.md> "<command>"
-    python -m transformer_head_scaled_amd.profsum traffic <fetch_dir> <write_dir> \
-        <copy_fetch_dir> <copy_write_dir> <out.json> "<commands>"
+    python -m transformer_head_scaled_amd.profsum traffic <copy_fetch_dir> <copy_write_dir> \
+        <out.json> "<commands>" bench=<fetch_dir>,<write_dir> [label=<fetch_dir>,<write_dir> ...]
 
     python -m transformer_head_scaled_amd.profsum counters <pmc_dir> <out.md> "<command>"
 
 ``stats`` turns a ``--kernel-trace --stats`` kernel_stats.csv into a markdown
 table.  ``counters`` turns one ``--pmc`` run of the SQ/GRBM counters below
-into per-kernel utilisation figures.  ``traffic`` reads four ``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE,
-for the attention bench and for a plain device copy of known size), scales
-each counter by known-bytes / counter-reading of the copy, and records the
-HBM bytes per attention launch together with a hash of the kernel source the
+into per-kernel utilisation figures.  ``traffic`` reads pairs of ``--pmc``
+runs (FETCH_SIZE, then WRITE_SIZE), one pair for a plain device copy of
+known size and one per workload group (the bench's two attention launches;
+the smaller workloads), scales each counter by known-bytes /
+counter-reading of the copy, and records the HBM bytes per launch of every
+libmha kernel together with a hash of the attention kernel's source the
 counters were taken on (the bench only reports the figure while the source
 is unchanged).
 """
@@ -139,9 +141,11 @@ def counters_md(run_dir, out_md, command, top=10):
     return rows
 
 
-def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json, commands):
-    f = counter_means(fetch_dir, "FETCH_SIZE")
-    w = counter_means(write_dir, "WRITE_SIZE")
+def traffic(cfetch_dir, cwrite_dir, out_json, commands, runs):
+    """runs: {label: (fetch_dir, write_dir)}, one pair of --pmc runs per
+    workload group.  Every libmha kernel's FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch, mean over its dispatches in that run), scaled by the bytes per
+    counter unit of a plain device copy of known size."""
     cf = counter_means(cfetch_dir, "FETCH_SIZE")
     cw = counter_means(cwrite_dir, "WRITE_SIZE")
     copy_name = max(cf, key=lambda k: cf[k])  # the 512 MiB copy dominates
@@ -150,23 +154,26 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json, commands):
     res = {"kernel_source_sha256_16": kernel_hash(), "copy_kernel": copy_name,
            "copy_bytes": COPY_BYTES, "fetch_size_kib_per_copy": cf[copy_name],
            "write_size_kib_per_copy": cw[copy_name], "fetch_factor": fetch_factor,
-           "write_factor": write_factor, "kernels": {}, "commands": commands}
-    for name in f:
-        if "sdpa_fwd" not in name:
-            continue
-        fb = f[name] * 1024.0 * fetch_factor
-        wb = w.get(name, 0.0) * 1024.0 * write_factor
-        res["kernels"][name] = {"fetch_kib": f[name], "write_kib": w.get(name),
-                                "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
-    # the bench workload is the largest launch of each mode among the d = 64
-    # kernels without key split or window (template arguments: dtype, d,
-    # causal, waves, key split, window, pair layout); smaller launches of
-    # other workloads may be in the same run
+           "write_factor": write_factor, "runs": {}, "commands": commands}
+    for label, (fetch_dir, write_dir) in runs.items():
+        f = counter_means(fetch_dir, "FETCH_SIZE")
+        w = counter_means(write_dir, "WRITE_SIZE")
+        ks = {}
+        for name in f:
+            if "mha::" not in name:
+                continue
+            fb = f[name] * 1024.0 * fetch_factor
+            wb = w.get(name, 0.0) * 1024.0 * write_factor
+            ks[name] = {"fetch_kib": f[name], "write_kib": w.get(name), "fetch_bytes": fb,
+                        "write_bytes": wb, "bytes_per_launch": fb + wb}
+        res["runs"][label] = ks
+    # the bench workload's kernels (template arguments: dtype, d, causal,
+    # waves, key split, window, pair layout), for bench.py's roofline
     targs = re.compile(r"sdpa_fwd_kernel<(\d+), (\d+), (true|false), (\d+), (true|false), "
                        r"(true|false)(?:, (?:true|false))?>")
     for mode, causal in (("noncausal", "false"), ("causal", "true")):
         cands = []
-        for k, v in res["kernels"].items():
+        for k, v in res["runs"].get("bench", {}).items():
             m = targs.search(k)
             if m and m.group(2) == "64" and m.group(3) == causal and m.group(5) == "false" \
                     and m.group(6) == "false":
@@ -185,6 +192,11 @@ if __name__ == "__main__":
     elif sys.argv[1] == "counters":
         counters_md(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "traffic":
-        print(json.dumps(traffic(*sys.argv[2:7], sys.argv[7]), indent=1))
+        # traffic <copy_fetch_dir> <copy_write_dir> <out.json> "<commands>" label=fetch_dir,write_dir ...
+        runs = {}
+        for spec in sys.argv[6:]:
+            label, dirs = spec.split("=", 1)
+            runs[label] = tuple(dirs.split(","))
+        print(json.dumps(traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], runs), indent=1))
     else:
         raise SystemExit(__doc__)
