@@ -565,6 +565,33 @@ def test_repeatable_bitwise():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("shape,mask", [
+    ((8, 8, 2048, 64), "none"),      # two-block layout, eight waves
+    ((2, 8, 2048, 64), "causal"),    # pair layout
+    ((4, 4, 640, 64), "none"),       # unmasked pair layout
+    ((3, 2, 1000, 32), "causal"),    # two-block causal layout (blocks u, nb - 1 - u)
+    ((8, 4, 3, 1500, 64), "none"),   # key split (n_q 3 against 1500 keys)
+])
+def test_bitwise_same_in_reversed_workgroup_order(shape, mask, monkeypatch):
+    """Each output row is produced by one workgroup in a fixed order of
+    operations, so launching the workgroups in the opposite order
+    (MHA_GRID_ORDER=reverse) gives bitwise the same result."""
+    if len(shape) == 5:
+        B, h, n_q, n_k, d = shape
+    else:
+        B, h, n_q, d = shape
+        n_k = n_q
+    ins = synth.sdpa_inputs(13, B, h, n_q, n_k, d, dtype="bf16")
+    tq, tk, tv = (to_dev(ins[n][0], "bf16") for n in "QKV")
+    note(f"grid order {shape} {mask}")
+    a = libmha.sdpa(tq, tk, tv, mask=mask)
+    monkeypatch.setenv("MHA_GRID_ORDER", "reverse")
+    b = libmha.sdpa(tq, tk, tv, mask=mask)
+    monkeypatch.delenv("MHA_GRID_ORDER")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 def test_output_guard_band():
     """The kernel writes exactly O: canary regions before and after it in
     the same allocation stay untouched."""
