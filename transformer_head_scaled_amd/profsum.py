@@ -5,6 +5,7 @@
         <out.json> "<commands>" bench=<fetch_dir>,<write_dir> [label=<fetch_dir>,<write_dir> ...]
 
     python -m transformer_head_scaled_amd.profsum counters <pmc_dir> <out.md> "<command>"
+    python -m transformer_head_scaled_amd.profsum traffic_md <traffic.json> <kernel_stats.csv> <out.md>
 
 ``stats`` turns a ``--kernel-trace --stats`` kernel_stats.csv into a markdown
 table.  ``counters`` turns one ``--pmc`` run of the SQ/GRBM counters below
@@ -186,9 +187,70 @@ def traffic(cfetch_dir, cwrite_dir, out_json, commands, runs):
     return res
 
 
+# Algorithmic HBM bytes per launch of the kernels the counter runs cover:
+# inputs read once plus outputs written once (bf16).  (run label, kernel
+# name fragment, what it is, bytes)
+def _cfg2_sdpa_bytes():
+    from transformer_head_scaled_amd import synth
+    _, lens = synth.workload_inputs(2)
+    h, n, d = 8, 64, 64
+    return 2 * (2 * 32 * h * n * d + 2 * h * d * int(lens.sum()))
+
+
+ALGORITHMIC = [
+    ("bench", "sdpa_fwd_kernel<1, 64, false, 8, false, false, false>", "[4,8,4096,64] unmasked", 67108864),
+    ("bench", "sdpa_fwd_kernel<1, 64, true, 8, false, false, true>", "[4,8,4096,64] causal", 67108864),
+    ("cfg3", "sdpa_fwd_kernel<1, 64, true, 4, false, false, true>", "[16,8,512,64] causal", 33554432),
+    ("cfg2", "sdpa_fwd_kernel<1, 64, false, 2, false, false, true>",
+     "[32,8,64,64] with key lengths (the visible K/V rows)", None),
+    ("cfg2", "gemm_kernel<1, 64, 64, 32, 32, 2>",
+     "base encoder projections, mean of the Q/K/V launch (2 MB x + 3·0.5 MB W + 3·2 MB out) "
+     "and the W^O launch (2 + 0.5 + 2 MB)", (2097152 + 3 * 524288 + 3 * 2097152 + 2 * 2097152 + 524288) // 2),
+    ("cfg4", "sdpa_fwd_kernel<1, 64, false, 8, false, false, true>", "[8,16,384→512,64]",
+     2 * (2 * 8 * 16 * 384 * 64 + 2 * 8 * 16 * 512 * 64)),
+    ("cfg4", "gemm_kernel<1, 128, 128, 64, 64, 2>",
+     "big cross-attention Q/K/V projections (x_q, x_kv, 3 W, Q/K/V out)",
+     2 * (3072 * 1024 + 4096 * 1024 + 3 * 1024 * 1024 + 3072 * 1024 + 2 * 4096 * 1024)),
+    ("cfg4", "gemm_kernel<1, 64, 64, 32, 32, 2>", "big cross-attention W^O (concat, W, out)",
+     2 * (3072 * 1024 + 1024 * 1024 + 3072 * 1024)),
+]
+
+
+def traffic_md(traffic_json, kernel_stats_csv, out_md):
+    """Counter bytes next to the algorithmic bytes, and both as GB/s over
+    the kernels' mean duration in the kernel trace."""
+    t = json.load(open(traffic_json))
+    durs = {r["Name"]: (float(r["AverageNs"]), float(r["MinNs"])) for r in read_stats(kernel_stats_csv)}
+    lines = ["# HBM traffic per launch: counters against algorithmic bytes", "",
+             "Counter bytes = FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what the same "
+             "counters read for a 512 MiB device copy (fetch x{:.3f}, write x{:.3f}); each workload "
+             "run alone, warm, so the reads include hits in the 256 MB last-level cache. Durations: "
+             "mean (min) of the kernel-trace summary, whose runs include cold-cache calls of the small "
+             "workloads. Commands: see sdpa_fwd_traffic.json and the kernel-statistics summary.".format(
+                 t["fetch_factor"], t["write_factor"]), "",
+             "| workload | kernel | counter MB | algorithmic MB | ratio | µs mean (min) | GB/s counters | GB/s algorithmic |",
+             "|---|---|---|---|---|---|---|---|"]
+    for label, frag, what, alg in ALGORITHMIC:
+        if alg is None:
+            alg = _cfg2_sdpa_bytes()
+        for name, v in t["runs"].get(label, {}).items():
+            if frag not in name:
+                continue
+            full = next((k for k in durs if frag in k), None)
+            mean_ns, min_ns = durs.get(full, (float("nan"), float("nan")))
+            b = v["bytes_per_launch"]
+            lines.append("| {} | `{}` | {:.2f} | {:.2f} | {:.2f} | {:.2f} ({:.2f}) | {:.0f} | {:.0f} |".format(
+                what, frag, b / 1e6, alg / 1e6, b / alg, mean_ns / 1e3, min_ns / 1e3, b / mean_ns,
+                alg / mean_ns))
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats_md(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "traffic_md":
+        traffic_md(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "counters":
         counters_md(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "traffic":
