@@ -164,7 +164,8 @@ enum {
   MHA_KERNEL_SPLIT = 3,   /* MFMA flash kernel, waves split the keys         */
   MHA_KERNEL_DECODE = 4,  /* one query row, no matrix cores                  */
   MHA_KERNEL_WINDOW = 5,  /* MFMA flash kernel, restricted window            */
-  MHA_KERNEL_WIDE = 6     /* d_k 256, 512: waves split the head dimension    */
+  MHA_KERNEL_WIDE = 6     /* d_k 256, 512: waves split the head dimension; 8
+                             waves (causal d_k 512): two groups split keys   */
 };
 typedef struct {
   int32_t kernel, waves, rows_per_workgroup, mask_kind;

@@ -258,6 +258,25 @@ def test_wide_heads(dtype, d, case):
     _check(got, exp, dtype, f"{dtype} wide d={d} {case}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [256, 512])
+def test_wide_causal_long(dtype, d):
+    """Causal wide heads over many key tiles: [2,2,1000,1000] with key lengths
+    (1000, 777): at d 512 each row block's key tiles are split between two
+    wave groups (odd tile counts, groups without a last tile, rows past the
+    key length) and the two partial results merged.  Every output."""
+    lens = [1000, 777]
+    scale = 1 / math.sqrt(d)
+    r = libmha.sdpa_route(libmha.MHA_BF16 if dtype == "bf16" else libmha.MHA_F16, 2, 2, 1000, 1000, d,
+                          mask="causal")
+    assert (r["kernel"], r["waves"]) == ("wide", 8 if d == 512 else 4), r
+    ins = synth.sdpa_inputs(960 + d, 2, 2, 1000, 1000, d, dtype=dtype)
+    note(f"sdpa {dtype} wide causal d={d} [2,2,1000,1000] lens {lens}")
+    got = _run(ins, dtype, "causal", lens, scale=scale)
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], scale, oracle.MASK_CAUSAL, lens)
+    _check(got, exp, dtype, f"{dtype} wide causal d={d} long")
+
+
 @pytest.mark.parametrize("d", [16, 32, 128])
 @pytest.mark.parametrize("mask", ["none", "causal"])
 def test_head_dims_four_wave(d, mask):

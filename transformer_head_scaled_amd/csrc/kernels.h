@@ -57,8 +57,13 @@ hipError_t launch_sdpa(const SdpaArgs& a, const SdpaRoute& r, int dtype, int cau
                        float scale, hipStream_t st);
 // the flash kernel's window form (bf16 / fp16), sdpa_window.hip
 hipError_t launch_sdpa_window(const SdpaArgs& a, const SdpaRoute& r, int dtype, int d, hipStream_t st);
-// wide heads, d = 256 or 512 (bf16 / fp16, no window), sdpa_wide.hip
-hipError_t launch_sdpa_wide(const SdpaArgs& a, int dtype, int causal, int d, hipStream_t st);
+// wide heads, d = 256 or 512 (bf16 / fp16, no window), sdpa_wide.hip; 8
+// waves: causal with the key tiles split between two groups of 4
+hipError_t launch_sdpa_wide(const SdpaArgs& a, int dtype, int causal, int d, int waves, hipStream_t st);
+// the smallest head dimension whose causal form splits the key tiles
+#ifndef SDPA_WIDE_SPLIT_MIN_D
+#define SDPA_WIDE_SPLIT_MIN_D 512
+#endif
 // one query row against a long key/value cache (bf16 / fp16, d = 64, 128,
 // no mask but key lengths), sdpa_decode.hip
 hipError_t launch_sdpa_decode(const SdpaArgs& a, int dtype, int d, hipStream_t st);

@@ -107,7 +107,9 @@ SdpaRoute sdpa_route(int dtype, bool causal, bool window, int64_t B, int64_t H, 
   if (dtype == MHA_F32) {
     r.kernel = SDPA_K_F32, r.waves = 1, r.rows = 64;
   } else if (d > 128) {
-    r.kernel = SDPA_K_WIDE, r.waves = 4, r.rows = 32;
+    // causal, wide enough: the key tiles split between two groups (the
+    // merge costs more than the split gains at d = 256)
+    r.kernel = SDPA_K_WIDE, r.waves = (causal && d >= SDPA_WIDE_SPLIT_MIN_D) ? 8 : 4, r.rows = 32;
   } else if (window) {
     int w = blocks_waves(n_q, heads);
     if (w > 2 && win_left + win_right < 2048) w = 2;

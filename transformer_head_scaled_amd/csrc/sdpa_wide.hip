@@ -37,8 +37,11 @@ namespace mha {
 
 namespace {
 
-template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
+// KS key groups of NW waves: KS = 2 splits a block's key tiles between two
+// groups (even and odd tiles), each with its own LDS buffers, and merges the
+// two partial results at the end.
+template <int DT, int D, bool CAUSAL, int KS = 1>
+__global__ __launch_bounds__(256 * KS) void sdpa_wide_kernel(SdpaArgs p) {
   constexpr int NW = 4, BN = 32;
   constexpr int DS = D / NW;         // columns per wave
   constexpr int NST = DS / 16;       // 16-deep MFMA steps of a partial score block
@@ -49,12 +52,12 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
 
   // one K and one V tile: 80 KB in all at d = 512 (48 KB at d = 256), so
   // that two (three) workgroups share a compute unit
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KS][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[KS][BN * D];
   // partial scores: lane l's 16 values as four 16-byte chunks, chunk c
   // stored at c ^ ((l >> 2) & 3) (the 16 lanes of a 16-byte access phase
   // then cover all 64 banks)
-  __shared__ __attribute__((aligned(16))) float Sx[NW][64 * 16];
+  __shared__ __attribute__((aligned(16))) float Sx[KS][NW][64 * 16];
   constexpr float kAccept = 256.f;
 
   const int nqb = (p.n_q + 31) / 32;
@@ -64,7 +67,9 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
   const int bh = (int)(blockIdx.x % nbh);
   const int b = bh / p.H, hh = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // (the wave index within its key group: it selects the columns)
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = KS == 1 ? 0 : wave_all / NW, wave = KS == 1 ? wave_all : wave_all % NW;
   const int l32 = lane & 31, hi = lane >> 5;
   const int row0 = qb * 32;
 
@@ -130,7 +135,7 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
       const int r = wave * CPW + i;
       load_lds_b128(krs,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-                        __attribute__((address_space(3))) void*)&Ks[r * 512]),
+                        __attribute__((address_space(3))) void*)&Ks[grp][r * 512]),
                     piece_src(r, false) + (uint32_t)(tile * BN * p.k_sr * 2));
     }
   };
@@ -140,14 +145,14 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
       const int r = wave * CPW + i;
       load_lds_b128(vrs,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-                        __attribute__((address_space(3))) void*)&Vs[r * 512]),
+                        __attribute__((address_space(3))) void*)&Vs[grp][r * 512]),
                     piece_src(r, true) + (uint32_t)(tile * BN * p.v_sr * 2));
     }
   };
   // K fragment st of this wave: key l32, chunk (wave·DS)/8 + 2·st + hi
   auto kfrag = [&](int st) __attribute__((always_inline)) {
     const int ch = (wave * DS) / 8 + 2 * st + hi;
-    return *(const u32x4*)&Ks[l32 * D + ((ch ^ (l32 & 15)) * 8)];
+    return *(const u32x4*)&Ks[grp][l32 * D + ((ch ^ (l32 & 15)) * 8)];
   };
   // Vᵀ fragment (t2, db): d = wave·DS + db·32 + l32, keys of the 16-key step
   // t2 in the score-register order, two transposing reads of 4 keys
@@ -161,7 +166,7 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
       const int key = t2 * 16 + 8 * e + v_key_l;
       const int d = wave * DS + db * 32 + v_col;
       const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)&Vs[key * D + (((d >> 3) ^ (4 * (key & 3))) * 8) + (d & 7)]);
+          (lds_s16x4*)&Vs[grp][key * D + (((d >> 3) ^ (4 * (key & 3))) * 8) + (d & 7)]);
       const u32x2 w = __builtin_bit_cast(u32x2, v);
       r[2 * e] = w[0];
       r[2 * e + 1] = w[1];
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
   auto put_sx = [&](const f32x16& sp) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *(f32x4*)&Sx[wave][lane * 16 + 4 * (q ^ sx_sw)] =
+      *(f32x4*)&Sx[grp][wave][lane * 16 + 4 * (q ^ sx_sw)] =
           f32x4{sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]};
   };
   // the full scores: the four partials, added in wave order
@@ -188,8 +193,8 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int at = lane * 16 + 4 * (q ^ sx_sw);
-      const f32x4 v = ((*(const f32x4*)&Sx[0][at] + *(const f32x4*)&Sx[1][at]) +
-                       *(const f32x4*)&Sx[2][at]) + *(const f32x4*)&Sx[3][at];
+      const f32x4 v = ((*(const f32x4*)&Sx[grp][0][at] + *(const f32x4*)&Sx[grp][1][at]) +
+                       *(const f32x4*)&Sx[grp][2][at]) + *(const f32x4*)&Sx[grp][3][at];
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[4 * q + e] = v[e];
     }
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d = wave * DS + db * 32 + 8 * g + 4 * hi;
-          const u32x2 w = *(const u32x2*)&Vs[k * D + (((d >> 3) ^ (4 * (k & 3))) * 8) + (d & 7)];
+          const u32x2 w = *(const u32x2*)&Vs[grp][k * D + (((d >> 3) ^ (4 * (k & 3))) * 8) + (d & 7)];
           const f32x4 x = unpack4<DT>(w);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -310,26 +315,90 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
   // unit fill the waits.  (Two stages of K and V, with or without forming
   // the next tile's partials during the softmax, measured 4-43 % slower:
   // they leave room for one workgroup less.)
-  if (ntiles > 0) {
-    gload_k(0);
-    gload_v(0);
+  // group grp takes the tiles grp, grp + KS, ...; both groups run the same
+  // number of steps (two workgroup barriers each), a group past its last
+  // tile only taking part in the barriers
+  const int niter = (ntiles + KS - 1) / KS;
+  if (grp < ntiles) {
+    gload_k(grp);
+    gload_v(grp);
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   asm volatile("s_barrier" ::: "memory");
-  for (int j = 0; j < ntiles; ++j) {
-    put_sx(spart());
+  for (int it = 0; it < niter; ++it) {
+    const int j = grp + KS * it;
+    const bool mine = KS == 1 || j < ntiles;
+    if (mine) put_sx(spart());
     // exchange writes visible, V(j) landed, every wave past its K reads
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-    if (j + 1 < ntiles) gload_k(j + 1);
-    f32x16 s = get_sx();
-    uint32_t pw[8];
-    softmax(s, j, pw);
-    pv(j, pw);
-    // K(j + 1) landed, every wave past its V and exchange reads
+    if (j + KS < ntiles) gload_k(j + KS);
+    if (mine) {
+      f32x16 s = get_sx();
+      uint32_t pw[8];
+      softmax(s, j, pw);
+      pv(j, pw);
+    }
+    // K(j + KS) landed, every wave past its V and exchange reads
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-    if (j + 1 < ntiles) gload_v(j + 1);
+    if (j + KS < ntiles) gload_v(j + KS);
+  }
+
+  if constexpr (KS == 2) {
+    // Merge: group 1 leaves its reference value (m·c, -inf without a tile),
+    // per-lane row sums and unnormalised columns in its LDS buffers; group 0
+    // rescales both parts to the larger reference value (the rescale of the
+    // online softmax) and adds them.  Every wave is past its last LDS read
+    // (the loop ends with a barrier).
+    constexpr int NO = 16 * NDB;
+    static_assert(NW * NO * 64 * 4 <= (int)(sizeof(Ks[0]) + sizeof(Vs[0])) &&
+                  NW * 2 * 64 * 4 <= (int)sizeof(Sx[0]), "merge area");
+    float* xo = (float*)&Ks[1][0];  // then Vs[1] where Ks[1] is too small
+    float* xm = &Sx[1][0][0];
+    if (grp == 1) {
+      if constexpr (NW * NO * 64 * 4 <= (int)sizeof(Ks[0])) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xo[((wave * NO) + 16 * db + i) * 64 + lane] = o[db][i];
+      } else {
+        float* xv = (float*)&Vs[1][0];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int at = ((wave * NO) + 16 * db + i) * 64 + lane;
+            constexpr int HALF = (int)sizeof(Ks[0]) / 4;
+            if (at < HALF) xo[at] = o[db][i]; else xv[at - HALF] = o[db][i];
+          }
+      }
+      xm[(wave * 2) * 64 + lane] = m == -INFINITY ? -INFINITY : mc;
+      xm[(wave * 2 + 1) * 64 + lane] = l;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    if (grp == 1) return;
+    const float m1 = xm[(wave * 2) * 64 + lane];
+    const float m0 = m == -INFINITY ? -INFINITY : mc;
+    const float M = fmaxf(m0, m1);
+    const float w0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
+    const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+    l = w0 * l + w1 * xm[(wave * 2 + 1) * 64 + lane];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int at = ((wave * NO) + 16 * db + i) * 64 + lane;
+        constexpr int HALF = (int)sizeof(Ks[0]) / 4;
+        float x1;
+        if constexpr (NW * NO * 64 * 4 <= (int)sizeof(Ks[0])) {
+          x1 = xo[at];
+        } else {
+          x1 = at < HALF ? xo[at] : ((float*)&Vs[1][0])[at - HALF];
+        }
+        o[db][i] = w0 * o[db][i] + w1 * x1;
+      }
   }
 
   // normalise and store this wave's columns of the lane's row
@@ -351,9 +420,17 @@ __global__ __launch_bounds__(256) void sdpa_wide_kernel(SdpaArgs p) {
 }
 
 template <int DT, int D>
-hipError_t launch_d(const SdpaArgs& a, int causal, hipStream_t st) {
+hipError_t launch_d(const SdpaArgs& a, int causal, int waves, hipStream_t st) {
   const int64_t grid = (a.n_q + 31) / 32 * (int64_t)a.B * a.H;
-  if (causal)
+  if constexpr (D >= SDPA_WIDE_SPLIT_MIN_D) {
+    if (causal && waves == 8) {
+      hipLaunchKernelGGL((sdpa_wide_kernel<DT, D, true, 2>), dim3((unsigned)grid), dim3(512), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  if (waves != 4)
+    return hipErrorInvalidValue;
+  else if (causal)
     hipLaunchKernelGGL((sdpa_wide_kernel<DT, D, true>), dim3((unsigned)grid), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((sdpa_wide_kernel<DT, D, false>), dim3((unsigned)grid), dim3(256), 0, st, a);
@@ -362,14 +439,14 @@ hipError_t launch_d(const SdpaArgs& a, int causal, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_sdpa_wide(const SdpaArgs& a, int dtype, int causal, int d, hipStream_t st) {
+hipError_t launch_sdpa_wide(const SdpaArgs& a, int dtype, int causal, int d, int waves, hipStream_t st) {
   if (a.window) return hipErrorInvalidValue;  // not offered for wide heads
   if (dtype == DT_BF16) {
-    if (d == 256) return launch_d<DT_BF16, 256>(a, causal, st);
-    if (d == 512) return launch_d<DT_BF16, 512>(a, causal, st);
+    if (d == 256) return launch_d<DT_BF16, 256>(a, causal, waves, st);
+    if (d == 512) return launch_d<DT_BF16, 512>(a, causal, waves, st);
   } else if (dtype == DT_F16) {
-    if (d == 256) return launch_d<DT_F16, 256>(a, causal, st);
-    if (d == 512) return launch_d<DT_F16, 512>(a, causal, st);
+    if (d == 256) return launch_d<DT_F16, 256>(a, causal, waves, st);
+    if (d == 512) return launch_d<DT_F16, 512>(a, causal, waves, st);
   }
   return hipErrorInvalidValue;
 }
