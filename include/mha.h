@@ -157,7 +157,7 @@ int mha_sdpa_window_strided(const void* Q, const void* K, const void* V, void* O
  * runs as the causal mask).
  */
 enum {
-  MHA_KERNEL_F32 = 0,     /* fp32, one thread per query row                  */
+  MHA_KERNEL_F32 = 0,     /* fp32, one or four lanes per query row           */
   MHA_KERNEL_BLOCKS = 1,  /* MFMA flash kernel, two 32-row blocks per wave   */
   MHA_KERNEL_PAIRS = 2,   /* MFMA flash kernel, one 32-row block per wave,
                              two key tiles per step                          */

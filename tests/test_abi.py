@@ -170,6 +170,8 @@ def test_strided_accepts_views_and_broadcast():
 ROUTES = [
     # (dtype, B, h, n_q, n_k, d, mask, window) -> (kernel, waves, workgroups or None)
     ((M.MHA_F32, 1, 1, 16, 16, 64, "none", None), ("f32", 1, 1)),          # single head fp32
+    ((M.MHA_F32, 1, 2, 70, 70, 64, "none", None), ("f32", 1, 10)),         # four lanes a row
+    ((M.MHA_F32, 16, 64, 70, 70, 64, "causal", None), ("f32", 1, 2048)),   # one lane a row
     ((M.MHA_BF16, 32, 8, 64, 64, 64, "none", None), ("pairs", 2, 256)),    # base encoder sub-layer
     ((M.MHA_BF16, 16, 8, 512, 512, 64, "causal", None), ("pairs", 4, 512)),  # decoder causal
     ((M.MHA_BF16, 8, 16, 384, 512, 64, "none", None), ("pairs", 8, 256)),  # big cross-attention

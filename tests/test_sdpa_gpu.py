@@ -204,6 +204,22 @@ def test_f32_head_dims(d):
     _check(got, exp, "f32", f"f32 d={d}")
 
 
+@pytest.mark.parametrize("d,mask", [(16, "none"), (64, "causal"), (128, "none")])
+def test_f32_lanes_per_row(d, mask):
+    """Both forms of the fp32 kernel: [1,2,70,70] takes four lanes a row
+    (16-row workgroups), [16,64,70,70] one lane a row (64-row workgroups,
+    enough of them to fill the SIMDs); key lengths ragged per batch."""
+    for B, h, rows in ((1, 2, 16), (16, 64, 64)):
+        r = libmha.sdpa_route(libmha.MHA_F32, B, h, 70, 70, d, mask=mask)
+        assert (r["kernel"], r["rows_per_workgroup"]) == ("f32", rows), r
+        lens = [(70 - 9 * i) % 71 for i in range(B)]
+        ins = synth.sdpa_inputs(1700 + d + B, B, h, 70, 70, d, dtype="f32")
+        note(f"sdpa f32 d={d} {mask} [{B},{h},70,70] rows/workgroup {rows}")
+        got = _run(ins, "f32", mask, lens, scale=1 / math.sqrt(d))
+        exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], 1 / math.sqrt(d), MASKS[mask], lens)
+        _check(got, exp, "f32", f"f32 d={d} {mask} [{B},{h},70,70]")
+
+
 # Head dimensions of Table 3 rows (A) and (C) of the nickwang.xyz page
 # (d_model fixed, h and d_k = d_v = d_model / h varied): the MFMA kernel for
 # each, on one- and two-wave workgroups, with ragged query blocks and key

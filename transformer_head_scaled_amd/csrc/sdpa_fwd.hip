@@ -11,23 +11,28 @@ namespace {
 
 // ---------------------------------------------------------------- fp32 path
 //
-// Plain fp32 attention for small problems and the 1e-5 parity case: one
-// thread per query row, K/V tiles of 32 keys broadcast from LDS, and the
-// online softmax taken one key at a time (the running max moves only when a
-// key beats it, and only then are O and the sum rescaled).  Any head
-// dimension in {16, 32, 64, 128}.  Inputs and the output accumulator are
-// fp32; each dot product, the running max and the exponent argument are
-// formed in fp64, so the scores carry no fp32 summation error even when they
-// are large (an unscaled softmax), and the only fp32 roundings left are expf
-// and the weighted sum of V.  The key loop is not unrolled: the query row and
-// the output row stay in registers and nothing spills.
-template <int DH>
+// Plain fp32 attention for small problems and the 1e-5 parity case: LPR
+// lanes per query row (1, or 4 where one lane a row would leave most SIMDs
+// idle), each holding DH / LPR of the row's columns of Q and O; K/V tiles of
+// 32 keys broadcast from LDS; the online softmax taken one key at a time (the
+// running max moves only when a key beats it, and only then are O and the
+// sum rescaled).  Any head dimension in {16, 32, 64, 128}.  Inputs and the
+// output accumulator are fp32; each dot product, the running max and the
+// exponent argument are formed in fp64 (four partial sums per lane, then the
+// LPR lanes' partials added pairwise, which gives the row's lanes identical
+// bits), so the scores carry no fp32 summation error even when they are
+// large (an unscaled softmax), and the only fp32 roundings left are expf and
+// the weighted sum of V.  The key loop is not unrolled: the row's registers
+// stay in registers and nothing spills.
+template <int DH, int LPR>
 __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, int causal) {
-  constexpr int TK = 32;
+  constexpr int TK = 32, DS = DH / LPR, RPW = 64 / LPR;  // columns per lane, rows per workgroup
+  static_assert(DS % 4 == 0, "four partial sums per lane");
   __shared__ __attribute__((aligned(16))) float Ks[TK * DH];
   __shared__ __attribute__((aligned(16))) float Vs[TK * DH];
   const int b = blockIdx.z, hh = blockIdx.y;
-  const int row = blockIdx.x * 64 + threadIdx.x;
+  const int row = blockIdx.x * RPW + (int)threadIdx.x / LPR;
+  const int c0 = ((int)threadIdx.x % LPR) * DS;  // this lane's first column
   const float* Qg = (const float*)p.Q + b * p.q_sb + hh * p.q_sh;
   const float* Kg = (const float*)p.K + b * p.k_sb + hh * p.k_sh;
   const float* Vg = (const float*)p.V + b * p.v_sb + hh * p.v_sh;
@@ -35,12 +40,13 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
 
   int n_eff = p.n_k;
   if (p.lens) n_eff = min(max(p.lens[b], 0), p.n_k);
+  const int r_end = min((int)(blockIdx.x + 1) * RPW, p.n_q);  // one past the block's last row
   int kend = n_eff;
-  if (causal) kend = min(kend, (int)(blockIdx.x + 1) * 64);
+  if (causal) kend = min(kend, r_end);
   int jlo = 0;  // restricted window: the keys the block's rows can reach
   if (p.window) {
-    kend = min(kend, min((int)(blockIdx.x + 1) * 64, p.n_q) - 1 + p.win_right + 1);
-    jlo = max(0, (int)blockIdx.x * 64 - p.win_left) / TK;
+    kend = min(kend, r_end - 1 + p.win_right + 1);
+    jlo = max(0, (int)blockIdx.x * RPW - p.win_left) / TK;
   }
   const int ntiles = kend > 0 ? (kend + TK - 1) / TK : 0;
   // this row's visible keys: [lo, hi)
@@ -51,10 +57,10 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
     hi = min(hi, row + p.win_right + 1);
   }
 
-  float q[DH], o[DH];
+  float q[DS], o[DS];
 #pragma unroll
-  for (int d = 0; d < DH; ++d) {
-    q[d] = row < p.n_q ? Qg[(int64_t)row * p.q_sr + d] : 0.f;
+  for (int d = 0; d < DS; ++d) {
+    q[d] = row < p.n_q ? Qg[(int64_t)row * p.q_sr + c0 + d] : 0.f;
     o[d] = 0.f;
   }
   double m = -INFINITY;
@@ -74,31 +80,39 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
     }
     __syncthreads();
     // a masked key is skipped outright (not added with weight 0), so the
-    // values it holds -- NaN included -- never reach this row
+    // values it holds -- NaN included -- never reach this row.  The bounds
+    // are the row's, the same for its LPR lanes, which therefore run the
+    // loop (and its lane exchanges) together.
     const int k0 = max(lo - j * TK, 0), k1 = min(hi - j * TK, TK);
 #pragma unroll 1
     for (int k = k0; k < k1; ++k) {
-      double acc = 0.0;
+      const float* kr = &Ks[k * DH + c0];
+      double a[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int d = 0; d < DH; ++d) acc = __builtin_fma((double)q[d], (double)Ks[k * DH + d], acc);
+      for (int d = 0; d < DS; ++d) a[d % 4] = __builtin_fma((double)q[d], (double)kr[d], a[d % 4]);
+      double acc = (a[0] + a[1]) + (a[2] + a[3]);
+      // x + partner(x) is the same sum on both lanes of a pair
+      if constexpr (LPR >= 2) acc += __shfl_xor(acc, 1, 64);
+      if constexpr (LPR >= 4) acc += __shfl_xor(acc, 2, 64);
       const double sc = acc * (double)scale;
       if (sc > m) {  // a new running max: rescale what has been summed
         const float alpha = (m == -INFINITY) ? 0.f : expf((float)(m - sc));
         l *= alpha;
 #pragma unroll
-        for (int d = 0; d < DH; ++d) o[d] *= alpha;
+        for (int d = 0; d < DS; ++d) o[d] *= alpha;
         m = sc;
       }
       const float e = expf((float)(sc - m));
       l += e;
+      const float* vr = &Vs[k * DH + c0];
 #pragma unroll
-      for (int d = 0; d < DH; ++d) o[d] = __builtin_fmaf(e, Vs[k * DH + d], o[d]);
+      for (int d = 0; d < DS; ++d) o[d] = __builtin_fmaf(e, vr[d], o[d]);
     }
   }
   if (row < p.n_q) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int d = 0; d < DH; ++d) Og[(int64_t)row * p.o_sr + d] = o[d] * inv;
+    for (int d = 0; d < DS; ++d) Og[(int64_t)row * p.o_sr + c0 + d] = o[d] * inv;
   }
 }
 
@@ -185,9 +199,14 @@ hipError_t launch_dim(const SdpaArgs& a, const SdpaRoute& r, int causal, int d, 
 }
 
 template <int DH>
-hipError_t launch_f32(const SdpaArgs& a, float scale, int causal, hipStream_t st) {
-  dim3 grid((unsigned)((a.n_q + 63) / 64), (unsigned)a.H, (unsigned)a.B);
-  hipLaunchKernelGGL((sdpa_f32_kernel<DH>), grid, dim3(64), 0, st, a, scale, causal);
+hipError_t launch_f32(const SdpaArgs& a, const SdpaRoute& r, float scale, int causal, hipStream_t st) {
+  dim3 grid((unsigned)((a.n_q + r.rows - 1) / r.rows), (unsigned)a.H, (unsigned)a.B);
+  if (r.rows == 16)
+    hipLaunchKernelGGL((sdpa_f32_kernel<DH, 4>), grid, dim3(64), 0, st, a, scale, causal);
+  else if (r.rows == 64)
+    hipLaunchKernelGGL((sdpa_f32_kernel<DH, 1>), grid, dim3(64), 0, st, a, scale, causal);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -199,10 +218,10 @@ hipError_t launch_sdpa(const SdpaArgs& a, const SdpaRoute& r, int dtype, int cau
     case SDPA_K_F32:
       if (dtype != DT_F32) break;
       switch (d) {
-        case 16: return launch_f32<16>(a, scale, causal, st);
-        case 32: return launch_f32<32>(a, scale, causal, st);
-        case 64: return launch_f32<64>(a, scale, causal, st);
-        case 128: return launch_f32<128>(a, scale, causal, st);
+        case 16: return launch_f32<16>(a, r, scale, causal, st);
+        case 32: return launch_f32<32>(a, r, scale, causal, st);
+        case 64: return launch_f32<64>(a, r, scale, causal, st);
+        case 128: return launch_f32<128>(a, r, scale, causal, st);
       }
       break;
     case SDPA_K_WIDE: return launch_sdpa_wide(a, dtype, causal, d, r.waves, st);

@@ -105,7 +105,9 @@ SdpaRoute sdpa_route(int dtype, bool causal, bool window, int64_t B, int64_t H, 
   const int64_t heads = B * H;
   SdpaRoute r{};
   if (dtype == MHA_F32) {
-    r.kernel = SDPA_K_F32, r.waves = 1, r.rows = 64;
+    // four lanes a row (16 rows a workgroup) where one lane a row would
+    // leave SIMDs without a workgroup
+    r.kernel = SDPA_K_F32, r.waves = 1, r.rows = heads * cdiv(n_q, 64) < kSimds ? 16 : 64;
   } else if (d > 128) {
     // causal, wide enough: the key tiles split between two groups (the
     // merge costs more than the split gains at d = 256)
