@@ -19,7 +19,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "transformer_head_scaled_amd", "csrc")
 BUILD = os.path.join(ROOT, "_build")
-KERNEL_OBJS = ["sdpa_fwd.o", "sdpa_window.o", "sdpa_wide.o", "sdpa_decode.o", "gemm_proj.o", "add_norm.o"]
+# the library's kernel objects: every .hip source of the build
+from transformer_head_scaled_amd.build import SOURCES  # noqa: E402
+KERNEL_OBJS = [os.path.splitext(s)[0] + ".o" for s in SOURCES if s.endswith(".hip")]
 HIPCC = "/opt/rocm/bin/hipcc"
 
 

@@ -112,6 +112,44 @@ def test_head_dims(case, dtype):
     _check(got, _oracle(ins, h, mask, lens), dtype, f"head dim {dm // h} {case}")
 
 
+# Short sequences (n_q, n_k <= 64, d_k = 64, no causal mask) run the Q/K/V
+# projections and the attention of each head in one launch.
+SHORT = [
+    # (B, n_q, n_k, d_model, h, cross, lens)
+    (4, 64, 64, 512, 8, False, [64, 63, 1, 0]),   # key lengths down to 0
+    (3, 50, 17, 256, 4, True, [17, 9, 0]),        # ragged rows and keys
+    (2, 33, 64, 1024, 16, True, None),            # sixteen k steps
+    (5, 7, 7, 64, 1, False, None),                # one head, one k step
+    (2, 64, 1, 128, 2, True, None),               # a single key
+]
+
+
+@pytest.mark.parametrize("case", SHORT, ids=lambda c: "x".join(map(str, c[:5])) + ("_cross" if c[5] else ""))
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_short_sequences(case, dtype):
+    B, n_q, n_k, dm, h, cross, lens = case
+    ins = synth.mha_inputs(300 + n_q + n_k + h, B, n_q, n_k, dm, h, cross, dtype=dtype)
+    note(f"forward {dtype} short {case}")
+    got = _run(ins, dtype, h, "none", lens, True)
+    _check(got, _oracle(ins, h, "none", lens), dtype, f"short {case}")
+
+
+def test_short_sequences_nan_padding():
+    """Cross-attention over padded encoder rows holding NaN and ±inf: the
+    rows at or past each key length never reach the output."""
+    B, n_q, n_k, dm, h = 3, 40, 64, 512, 8
+    lens = [64, 30, 5]
+    ins = synth.mha_inputs(377, B, n_q, n_k, dm, h, True)
+    xkv = np.array(ins["x_kv"][1], dtype=np.float32)
+    for b, n in enumerate(lens):
+        xkv[b, n:] = np.nan
+        xkv[b, n::3] = np.inf
+    ins["x_kv"] = synth.round_to(xkv, "bf16")
+    note("forward short, NaN/inf padding")
+    got = _run(ins, "bf16", h, "none", lens, True)
+    _check(got, _oracle(ins, h, "none", lens), "bf16", "short NaN padding")
+
+
 def test_single_head_equals_sdpa_chain():
     """h = 1 (Table 3 (A) of the nickwang.xyz page): one head of full width
     d_k = d_model, so the sublayer is one attention with scale 1/√d_model

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libmha.so")
 SOURCES = ["mha_api.cpp", "sdpa_route.cpp", "sdpa_fwd.hip", "sdpa_window.hip", "sdpa_wide.hip", "sdpa_decode.hip",
-           "gemm_proj.hip", "add_norm.hip"]
+           "gemm_proj.hip", "add_norm.hip", "mha_short.hip"]
 # Per-source flags.  The flash attention kernel is scheduled with LLVM's
 # "max-memory-clause" strategy: the same instructions and results, measured
 # (interleaved runs) 1-2 % faster causal at d 64 and 128 and 2 % unmasked at

@@ -96,6 +96,24 @@ struct GemmArgs {
 // Chooses the tile shape from the problem sizes.
 hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t st);
 
+// The Q/K/V projections and the attention of each (batch, head) in one
+// workgroup, for n_q, n_k in [1, 64], head dimension 64, no causal mask
+// (mha_short.hip).  x_q [B, n_q, d_model], x_kv [B, n_k, d_model] (the same
+// pointer as x_q with self set), W* [d_model, H·64]; C receives the concat
+// [B, n_q, H·64].  c = scale·log2(e).
+struct ShortArgs {
+  const void* xq;
+  const void* xkv;
+  const void* Wq;
+  const void* Wk;
+  const void* Wv;
+  void* C;
+  const int32_t* lens;  // device int32[B] valid key counts, or null
+  int32_t B, H, n_q, n_k, d_model, self;
+  float c;
+};
+hipError_t launch_mha_short(const ShortArgs& a, int dtype, hipStream_t st);
+
 // out = LayerNorm(x + sub) per row of d features (contiguous rows):
 // z_f32 = false: x and sub in the storage dtype; true: z already holds
 // x + sub in fp32.  gamma, beta [d] and out in the storage dtype.

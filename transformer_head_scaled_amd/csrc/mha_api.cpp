@@ -17,6 +17,13 @@
 
 #include "kernels.h"
 
+// mha_forward for n_q, n_k <= 64 at head dimension 64 without a causal mask:
+// 1 runs the projections and the attention of each head in one launch
+// (mha_short.hip), 0 keeps them separate
+#ifndef MHA_SHORT_FUSED
+#define MHA_SHORT_FUSED 1
+#endif
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -493,7 +500,10 @@ static int forward_impl(const char* fn, const void* x_q, const void* x_kv, const
     return p;
   };
   g.nprob = 0;
-  if (n_k > 0) {
+  // short sequences: projections and attention of each head in one launch
+  const bool fused = MHA_SHORT_FUSED && d == 64 && n_q <= 64 && n_k >= 1 && n_k <= 64 &&
+                     mask_kind == MHA_MASK_NONE;
+  if (n_k > 0 && !fused) {
     g.prob[g.nprob++] = split(x_q, Wq, q_ws, n_q);
     g.prob[g.nprob++] = split(xkv, Wk, k_ws, n_k);
     g.prob[g.nprob++] = split(xkv, Wv, v_ws, n_k);
@@ -502,14 +512,22 @@ static int forward_impl(const char* fn, const void* x_q, const void* x_kv, const
   if (trace_on())
     std::fprintf(stderr,
                  "[libmha] forward dtype=%d B=%lld n_q=%lld n_k=%lld d_model=%lld h=%d mask=%d "
-                 "lens=%s self=%d ws=%zu%s\n",
+                 "lens=%s self=%d ws=%zu%s%s\n",
                  (int)dtype, (long long)B, (long long)n_q, (long long)n_k, (long long)d_model,
                  (int)h, (int)mask_kind, kv_lens ? "yes" : "no", self ? 1 : 0, L.total,
-                 owned ? " (allocated)" : "");
+                 owned ? " (allocated)" : "", fused ? " fused projections+attention" : "");
   if (g.nprob) e = mha::launch_gemm(g, dtype, st);
 
+  if (fused) {  // (1) + (2) in one launch, into the concat
+    mha::ShortArgs a{};
+    a.xq = x_q, a.xkv = xkv, a.Wq = Wq, a.Wk = Wk, a.Wv = Wv, a.C = c_ws, a.lens = kv_lens;
+    a.B = (int32_t)B, a.H = h, a.n_q = (int32_t)n_q, a.n_k = (int32_t)n_k;
+    a.d_model = (int32_t)d_model, a.self = self ? 1 : 0;
+    a.c = (1.0f / std::sqrt((float)d)) * 1.4426950408889634f;
+    e = mha::launch_mha_short(a, dtype, st);
+  }
   // (2) attention per head; output in the concat layout [B, n_q, h·d]
-  if (e == hipSuccess) {
+  if (e == hipSuccess && !fused) {
     mha::SdpaArgs a{};
     a.Q = q_ws, a.K = k_ws, a.V = v_ws, a.O = c_ws;
     a.q_sr = d, a.q_sh = n_q * d, a.q_sb = h * n_q * d;
