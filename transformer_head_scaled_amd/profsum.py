@@ -190,22 +190,15 @@ def traffic(cfetch_dir, cwrite_dir, out_json, commands, runs):
 # Algorithmic HBM bytes per launch of the kernels the counter runs cover:
 # inputs read once plus outputs written once (bf16).  (run label, kernel
 # name fragment, what it is, bytes)
-def _cfg2_sdpa_bytes():
-    from transformer_head_scaled_amd import synth
-    _, lens = synth.workload_inputs(2)
-    h, n, d = 8, 64, 64
-    return 2 * (2 * 32 * h * n * d + 2 * h * d * int(lens.sum()))
-
-
 ALGORITHMIC = [
     ("bench", "sdpa_fwd_kernel<1, 64, false, 8, false, false, false>", "[4,8,4096,64] unmasked", 67108864),
     ("bench", "sdpa_fwd_kernel<1, 64, true, 8, false, false, true>", "[4,8,4096,64] causal", 67108864),
     ("cfg3", "sdpa_fwd_kernel<1, 64, true, 4, false, false, true>", "[16,8,512,64] causal", 33554432),
-    ("cfg2", "sdpa_fwd_kernel<1, 64, false, 2, false, false, true>",
-     "[32,8,64,64] with key lengths (the visible K/V rows)", None),
-    ("cfg2", "gemm_kernel<1, 64, 64, 32, 32, 2>",
-     "base encoder projections, mean of the Q/K/V launch (2 MB x + 3·0.5 MB W + 3·2 MB out) "
-     "and the W^O launch (2 + 0.5 + 2 MB)", (2097152 + 3 * 524288 + 3 * 2097152 + 2 * 2097152 + 524288) // 2),
+    ("cfg2", "mha_short_kernel<1, true, 4>",
+     "base encoder Q/K/V projections + attention, one launch (x 2 MB, W^Q/K/V 3·0.5 MB, concat 2 MB)",
+     2097152 + 3 * 524288 + 2097152),
+    ("cfg2", "gemm_kernel<1, 64, 64, 32, 32, 2>", "base encoder W^O (concat 2 MB, W 0.5 MB, out 2 MB)",
+     2 * 2097152 + 524288),
     ("cfg4", "sdpa_fwd_kernel<1, 64, false, 8, false, false, true>", "[8,16,384→512,64]",
      2 * (2 * 8 * 16 * 384 * 64 + 2 * 8 * 16 * 512 * 64)),
     ("cfg4", "gemm_kernel<1, 128, 128, 64, 64, 2>",
@@ -231,8 +224,6 @@ def traffic_md(traffic_json, kernel_stats_csv, out_md):
              "| workload | kernel | counter MB | algorithmic MB | ratio | µs mean (min) | GB/s counters | GB/s algorithmic |",
              "|---|---|---|---|---|---|---|---|"]
     for label, frag, what, alg in ALGORITHMIC:
-        if alg is None:
-            alg = _cfg2_sdpa_bytes()
         for name, v in t["runs"].get(label, {}).items():
             if frag not in name:
                 continue
