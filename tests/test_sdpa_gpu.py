@@ -195,6 +195,59 @@ def test_ragged(dtype, case):
     _check(got, exp, dtype, f"{dtype} {case}")
 
 
+# Keys up to the 2 GiB range of one head's K (and V) buffer: the key and
+# value rows are a random block of P rows (P prime) repeated R times, so
+# attention over all R·P keys is attention over one copy (every weight of a
+# copy appears R times and R cancels in the normalisation), which the oracle
+# computes on the block.  A 32-bit offset that wrapped (2^32 bytes = 2^25
+# rows, not a multiple of P) or a range that ended early would read other
+# rows.
+_P, _R = 65521, 255  # 255·65521 keys · 128 bytes = 99.6 % of 2^31 − 1
+
+
+@pytest.mark.parametrize("n_q,kernel", [(1, "decode"), (64, "split")])
+def test_keys_at_the_buffer_limit(n_q, kernel):
+    d = 64
+    n_k = _P * _R
+    assert n_k * d * 2 <= 2**31 - 1 and n_k * d * 2 > 0.99 * 2**31
+    r = libmha.sdpa_route(libmha.MHA_BF16, 1, 1, n_q, n_k, d)
+    assert r["kernel"] == kernel, r
+    ins = synth.sdpa_inputs(4242 + n_q, 1, 1, n_q, _P, d)
+    q = to_dev(ins["Q"][0], "bf16")
+    k = to_dev(np.tile(ins["K"][0], (1, 1, _R, 1)), "bf16")
+    v = to_dev(np.tile(ins["V"][0], (1, 1, _R, 1)), "bf16")
+    note(f"sdpa bf16 [1,1,{n_q},{n_k}] ({kernel} kernel), K and V {n_k * d * 2 / 2**30:.3f} GiB each")
+    for lens, copies in ((None, _R), ([200 * _P], 200)):
+        out = libmha.sdpa(q, k, v, scale=0.125, seq_lens=lens_dev(lens))
+        torch.cuda.synchronize()
+        got = from_dev(out)
+        exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], 0.125, oracle.MASK_NONE)
+        _check(got, exp, "bf16", f"[1,1,{n_q},{n_k}] {copies} copies of {_P} keys")
+    del k, v
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_long_sequence_sampled_rows(mask):
+    """[1,2,65536,64]: a thousand key tiles per row block; sampled rows
+    (both ends, tile and block boundaries, random) against the oracle on
+    exactly the keys each sees."""
+    B, h, n, d = 1, 2, 65536, 64
+    ins = synth.sdpa_inputs(65536, B, h, n, n, d)
+    note(f"sdpa bf16 [1,2,65536,64] {mask}")
+    got = _run(ins, "bf16", mask)
+    rng = np.random.default_rng(7)
+    rows = sorted(set([0, 1, 31, 32, 63, 64, 4095, 4096, 32767, 32768, n - 65, n - 64, n - 2, n - 1] +
+                      list(rng.integers(0, n, 12))))
+    Q, K, V = (ins[x][1] for x in "QKV")
+    for hh in range(h):
+        for r in rows:
+            kend = r + 1 if mask == "causal" else n
+            exp = oracle.sdpa(Q[:, hh:hh + 1, r:r + 1], K[:, hh:hh + 1, :kend], V[:, hh:hh + 1, :kend],
+                              0.125, oracle.MASK_NONE)
+            _check(got[:, hh:hh + 1, r:r + 1], exp, "bf16", f"[1,2,65536,64] {mask} head {hh} row {r}")
+
+
 @pytest.mark.parametrize("d", [16, 32, 128])
 def test_f32_head_dims(d):
     ins = synth.sdpa_inputs(7, 2, 2, 70, 45, d, dtype="f32")
