@@ -17,7 +17,11 @@
 // head split / concat is folded into the store address (see GemmProblem).
 //
 // Tiles: TM × TN outputs per workgroup of 4 waves (2 × 2, each TM/2 × TN/2),
-// 64 k per stage, two LDS stages.  A and W tiles go from memory straight
+// two LDS stages of 64 k (64 × 64 tiles) or 32 k (128 × 128 tiles: 32 KB of
+// LDS, so three workgroups share a compute unit where 64 k left room for two;
+// the big cross-attention's Q/K/V launch then runs its 704 tiles in one
+// round, measured 1.5-2 % faster on its sub-layer, identical results).
+// A and W tiles go from memory straight
 // into LDS (buffer loads with an LDS destination; the buffer range ends at
 // row M of A, so rows past it read as zero).  LDS rows are stored with
 // their 16-byte chunks XOR-permuted by row bits so that every fragment read
@@ -33,7 +37,9 @@ namespace mha {
 
 namespace {
 
-constexpr int BK = 64;  // k per LDS stage (four 16-k MFMA steps); A rows are 128 bytes
+#ifndef GEMM_BK_128
+#define GEMM_BK_128 32  // k per LDS stage of the 128 x 128 tiles
+#endif
 
 #ifndef GEMM_STAGES_128
 #define GEMM_STAGES_128 2
@@ -58,16 +64,18 @@ constexpr int BK = 64;  // k per LDS stage (four 16-k MFMA steps); A rows are 12
 #endif
 
 // TM x TN outputs per workgroup; each wave computes WTM x WTN of them.
-template <int DT, int TM, int TN, int WTM, int WTN, int NSTAGE>
+// BK: k per LDS stage (BK / 16 MFMA steps; A rows of 2·BK bytes).
+template <int DT, int TM, int TN, int WTM, int WTN, int NSTAGE, int BK>
 __global__ __launch_bounds__((TM / WTM) * (TN / WTN) * 64) void gemm_kernel(GemmArgs g) {
   constexpr int NWN = TN / WTN;              // waves along n
   constexpr int NWAVES = (TM / WTM) * NWN;
   constexpr int WM = WTM / 32;               // 32-row m blocks per wave
   constexpr int WN = WTN / 32;               // 32-col n blocks per wave
-  constexpr int ACH = TM * 128 / 1024 / NWAVES;     // 1 KB A pieces per wave and stage
+  constexpr int ACR = BK / 8;                        // 16-byte chunks per A row
+  constexpr int ACH = TM * BK * 2 / 1024 / NWAVES;   // 1 KB A pieces per wave and stage
   constexpr int WCH = BK * TN * 2 / 1024 / NWAVES;  // 1 KB W pieces per wave and stage
   constexpr int WCR = TN / 8;         // 16-byte chunks per W row
-  static_assert(ACH >= 1 && WCH >= 1 && (TN == 64 || TN == 128), "tile shape");
+  static_assert(ACH >= 1 && WCH >= 1 && (TN == 64 || TN == 128) && (BK == 32 || BK == 64), "tile shape");
 
   __shared__ __attribute__((aligned(16))) uint16_t As[NSTAGE][TM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t Ws[NSTAGE][BK * TN];
@@ -88,10 +96,12 @@ __global__ __launch_bounds__((TM / WTM) * (TN / WTN) * 64) void gemm_kernel(Gemm
   const int l32 = lane & 31, hi = lane >> 5, i16 = lane & 15, g16 = (lane >> 4) & 1;
   const int wm = wave / NWN, wn = wave % NWN;
 
-  // chunk permutations: A rows (128 bytes) by bits 1..3 of the row; W rows
+  // chunk permutations: A rows (ACR chunks) by the row's index among the
+  // rows of one 256-byte bank cycle (16 / ACR of them), so that 16 lanes
+  // reading one chunk index of 16 consecutive rows cover all banks; W rows
   // (128 or 256 bytes) by the row's position among 4 consecutive k, so that
   // the 4 (or 2 x 4) rows a transposing read touches fall on distinct banks
-  auto a_swz = [](int m) { return (m >> 1) & 7; };
+  auto a_swz = [](int m) { return (m / (16 / ACR)) & (ACR - 1); };
   auto w_swz = [](int k) { return TN == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); };
 
   // A: descriptor over this workgroup's rows; per lane, the byte offset of
@@ -103,8 +113,8 @@ __global__ __launch_bounds__((TM / WTM) * (TN / WTN) * 64) void gemm_kernel(Gemm
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
     const int q = (wave * ACH + i) * 64 + lane;  // LDS chunk this lane fills
-    const int m = q >> 3;
-    a_off[i] = (uint32_t)(m * P.lda * 2 + ((q & 7) ^ a_swz(m)) * 16);
+    const int m = q / ACR;
+    a_off[i] = (uint32_t)(m * P.lda * 2 + ((q % ACR) ^ a_swz(m)) * 16);
   }
   uint32_t w_off[WCH];
 #pragma unroll
@@ -260,8 +270,9 @@ __global__ __launch_bounds__((TM / WTM) * (TN / WTN) * 64) void gemm_kernel(Gemm
   }
 }
 
-template <int DT, int TM, int TN, int WTM, int WTN, int NSTAGE>
+template <int DT, int TM, int TN, int WTM, int WTN, int NSTAGE, int BK = 64>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
+  if (a.K % BK != 0) return hipErrorInvalidValue;
   int max_tiles = 0;
   for (int i = 0; i < a.nprob; ++i) {
     const int t = ((a.prob[i].M + TM - 1) / TM) * (a.N / TN);
@@ -269,7 +280,7 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   }
   if (max_tiles == 0) return hipSuccess;
   constexpr int threads = (TM / WTM) * (TN / WTN) * 64;
-  hipLaunchKernelGGL((gemm_kernel<DT, TM, TN, WTM, WTN, NSTAGE>), dim3(max_tiles, a.nprob), dim3(threads), 0,
+  hipLaunchKernelGGL((gemm_kernel<DT, TM, TN, WTM, WTN, NSTAGE, BK>), dim3(max_tiles, a.nprob), dim3(threads), 0,
                      st, a);
   return hipGetLastError();
 }
@@ -286,14 +297,14 @@ hipError_t launch_dt(const GemmArgs& a, hipStream_t st) {
   if (GEMM_HUGE && a.N % 128 == 0 && tiles(256, 128) >= GEMM_BIG_MIN)
     return launch_t<DT, 256, 128, 64, 64, GEMM_STAGES_HUGE>(a, st);  // measured slower so far: off by default
   if (a.N % 128 == 0 && tiles(128, 128) >= GEMM_BIG_MIN)
-    return launch_t<DT, 128, 128, GEMM_WTM_128, GEMM_WTN_128, GEMM_STAGES_128>(a, st);
+    return launch_t<DT, 128, 128, GEMM_WTM_128, GEMM_WTN_128, GEMM_STAGES_128, GEMM_BK_128>(a, st);
   return launch_t<DT, 64, 64, 32, 32, GEMM_STAGES_64>(a, st);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t st) {
-  if (a.N % 64 != 0 || a.K % BK != 0) return hipErrorInvalidValue;
+  if (a.N % 64 != 0 || a.K % 64 != 0) return hipErrorInvalidValue;
   return dtype == DT_BF16 ? launch_dt<DT_BF16>(a, st) : launch_dt<DT_F16>(a, st);
 }
 
