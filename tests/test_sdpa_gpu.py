@@ -442,6 +442,45 @@ def test_nonfinite_values_inside_masked_tiles(dtype, d):
         _check_nonfinite(got, exp, dtype, f"{dtype} d={d} causal non-finite values lens {lens}")
 
 
+@pytest.mark.parametrize("mask", ["none", "causal"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [16, 64, 128])
+def test_nonfinite_queries_and_keys(mask, dtype, d):
+    """[1,2,200,200] with a NaN query element (head 0, row 77), an infinite
+    element in the first key (head 0, key 0: a score of +∞ or −∞ by the sign
+    of the query element it meets, so some rows start from a −∞ score) and a
+    NaN key element (head 1, key 150): NaN exactly where the oracle has it
+    (the rows that see the NaN key or meet +∞, and row 77), every other
+    output within the tolerance."""
+    scale = 1 / math.sqrt(d)
+    ins = synth.sdpa_inputs(61 + d, 1, 2, 200, 200, d, dtype=dtype)
+    # row 0 of head 0 meets +∞ at key 0 (its only key under the causal mask:
+    # a row whose every visible score is −∞ is 0/0 in the exact softmax, a
+    # reading of its own, kept out here)
+    st, v64 = ins["Q"]
+    if v64[0, 0, 0, 3 % d] < 0:
+        v64[0, 0, 0, 3 % d] = -v64[0, 0, 0, 3 % d]
+        if dtype == "f32":
+            st[0, 0, 0, 3 % d] = -st[0, 0, 0, 3 % d]
+        else:
+            st.view(np.uint16)[0, 0, 0, 3 % d] ^= 0x8000
+    bits = {"bf16": {"nan": 0x7fc0, "inf": 0x7f80}, "f16": {"nan": 0x7e00, "inf": 0x7c00}}
+    for name, hh, row, col, kind in (("Q", 0, 77, 5 % d, "nan"), ("K", 0, 0, 3 % d, "inf"),
+                                     ("K", 1, 150, 7 % d, "nan")):
+        st, v64 = ins[name]
+        if dtype == "f32":
+            st[0, hh, row, col] = np.float32(np.nan if kind == "nan" else np.inf)
+        else:
+            st.view(np.uint16)[0, hh, row, col] = bits[dtype][kind]
+        v64[0, hh, row, col] = np.nan if kind == "nan" else np.inf
+    note(f"sdpa {dtype} d={d} {mask} [1,2,200,200] non-finite Q and K")
+    got = _run(ins, dtype, mask, scale=scale)
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], scale, MASKS[mask])
+    # some rows meet −∞ at key 0 and stay finite
+    assert np.isfinite(exp[0, 0, 1:, 0]).any()
+    _check_nonfinite(got, exp, dtype, f"{dtype} d={d} {mask} non-finite Q and K")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [16, 64, 128])
 def test_nonfinite_values_window_edges(dtype, d):

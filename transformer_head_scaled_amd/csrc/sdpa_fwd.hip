@@ -102,7 +102,9 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
         for (int d = 0; d < DS; ++d) o[d] *= alpha;
         m = sc;
       }
-      const float e = expf((float)(sc - m));
+      // a score of −∞ (an infinite key element) has weight 0, also while the
+      // running max is still −∞
+      const float e = sc == -INFINITY ? 0.f : expf((float)(sc - m));
       l += e;
       const float* vr = &Vs[k * DH + c0];
 #pragma unroll
