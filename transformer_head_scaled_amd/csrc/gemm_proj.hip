@@ -17,7 +17,8 @@
 // head split / concat is folded into the store address (see GemmProblem).
 //
 // Tiles: TM × TN outputs per workgroup of 4 waves (2 × 2, each TM/2 × TN/2),
-// two LDS stages of 64 k (64 × 64 tiles) or 32 k (128 × 128 tiles: 32 KB of
+// two LDS stages of 64 k (64 × 64 tiles; 128 k for grids of at most two
+// tiles a CU) or 32 k (128 × 128 tiles: 32 KB of
 // LDS, so three workgroups share a compute unit where 64 k left room for two;
 // the big cross-attention's Q/K/V launch then runs its 704 tiles in one
 // round, measured 1.5-2 % faster on its sub-layer, identical results).
@@ -39,6 +40,9 @@ namespace {
 
 #ifndef GEMM_BK_128
 #define GEMM_BK_128 32  // k per LDS stage of the 128 x 128 tiles
+#endif
+#ifndef GEMM_SMALL_GRID
+#define GEMM_SMALL_GRID 512  // 64 x 64 grids up to this many tiles (two a CU) take 128 k a stage
 #endif
 
 #ifndef GEMM_STAGES_128
@@ -75,7 +79,7 @@ __global__ __launch_bounds__((TM / WTM) * (TN / WTN) * 64) void gemm_kernel(Gemm
   constexpr int ACH = TM * BK * 2 / 1024 / NWAVES;   // 1 KB A pieces per wave and stage
   constexpr int WCH = BK * TN * 2 / 1024 / NWAVES;  // 1 KB W pieces per wave and stage
   constexpr int WCR = TN / 8;         // 16-byte chunks per W row
-  static_assert(ACH >= 1 && WCH >= 1 && (TN == 64 || TN == 128) && (BK == 32 || BK == 64), "tile shape");
+  static_assert(ACH >= 1 && WCH >= 1 && (TN == 64 || TN == 128) && (BK == 32 || BK == 64 || BK == 128), "tile shape");
 
   __shared__ __attribute__((aligned(16))) uint16_t As[NSTAGE][TM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t Ws[NSTAGE][BK * TN];
@@ -298,6 +302,12 @@ hipError_t launch_dt(const GemmArgs& a, hipStream_t st) {
     return launch_t<DT, 256, 128, 64, 64, GEMM_STAGES_HUGE>(a, st);  // measured slower so far: off by default
   if (a.N % 128 == 0 && tiles(128, 128) >= GEMM_BIG_MIN)
     return launch_t<DT, 128, 128, GEMM_WTM_128, GEMM_WTN_128, GEMM_STAGES_128, GEMM_BK_128>(a, st);
+  // 64 x 64 tiles: 128 k a stage (64 KB of LDS, two workgroups a CU, half
+  // the dependent load-and-multiply steps) where the grid fits at two a CU
+  // (the base encoder's W^O: 1.3 % on its sub-layer; the 768 tiles of the
+  // big cross-attention's W^O lost 4 % to the lower occupancy)
+  if (a.K % 128 == 0 && tiles(64, 64) <= GEMM_SMALL_GRID)
+    return launch_t<DT, 64, 64, 32, 32, GEMM_STAGES_64, 128>(a, st);
   return launch_t<DT, 64, 64, 32, 32, GEMM_STAGES_64>(a, st);
 }
 
