@@ -450,15 +450,14 @@ def test_nonfinite_queries_and_keys(mask, dtype, d):
     element in the first key (head 0, key 0: a score of +∞ or −∞ by the sign
     of the query element it meets, so some rows start from a −∞ score) and a
     NaN key element (head 1, key 150): NaN exactly where the oracle has it
-    (the rows that see the NaN key or meet +∞, and row 77), every other
-    output within the tolerance."""
+    (the rows that see the NaN key or meet +∞, row 77, and causal row 0,
+    whose only score is −∞), every other output within the tolerance."""
     scale = 1 / math.sqrt(d)
     ins = synth.sdpa_inputs(61 + d, 1, 2, 200, 200, d, dtype=dtype)
-    # row 0 of head 0 meets +∞ at key 0 (its only key under the causal mask:
-    # a row whose every visible score is −∞ is 0/0 in the exact softmax, a
-    # reading of its own, kept out here)
+    # row 0 of head 0 meets −∞ at key 0: under the causal mask its only key,
+    # so its softmax is 0/0 (NaN); unmasked, the other keys keep it finite
     st, v64 = ins["Q"]
-    if v64[0, 0, 0, 3 % d] < 0:
+    if v64[0, 0, 0, 3 % d] > 0:
         v64[0, 0, 0, 3 % d] = -v64[0, 0, 0, 3 % d]
         if dtype == "f32":
             st[0, 0, 0, 3 % d] = -st[0, 0, 0, 3 % d]

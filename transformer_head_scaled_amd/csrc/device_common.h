@@ -106,6 +106,15 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
 
+// 1 / (a row's weight sum), for the normalisation.  A sum of 0 means no
+// visible key (the row's output is 0) or, with visible keys, only scores of
+// −∞ among them -- infinite inputs; the exact softmax is then 0/0, NaN.  (A
+// visible key with a finite score adds exp2(0) = 1 to the sum: the largest
+// one is the reference value or beats it.)
+__device__ __forceinline__ float row_sum_inverse(float sum, bool visible) {
+  return sum > 0.f ? 1.f / sum : (visible ? __builtin_nanf("") : 0.f);
+}
+
 __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
                                             __builtin_bit_cast(uint32_t, x), false, false);

@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256) void mha_short_kernel(ShortArgs a) {
       }
   // normalise, store columns hh·64 + d of the concat row
   const float L = pair_sum(l);
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float inv = row_sum_inverse(L, n_eff > 0);
   if (row < a.n_q) {
     uint16_t* crow = (uint16_t*)a.C + ((int64_t)b * a.n_q + row) * ldw + hh * SN;
 #pragma unroll

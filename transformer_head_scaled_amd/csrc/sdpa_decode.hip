@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void sdpa_decode_kernel(SdpaArgs p)
     for (int e = 0; e < 8; ++e) o2[e] = xs[w][ch][2 + e];
     merge(xs[w][ch][0], xs[w][ch][1], o2);
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = row_sum_inverse(l, n_eff > 0);
   const u32x4 out = {pack2<DT>(o[0] * inv, o[1] * inv), pack2<DT>(o[2] * inv, o[3] * inv),
                      pack2<DT>(o[4] * inv, o[5] * inv), pack2<DT>(o[6] * inv, o[7] * inv)};
   uint16_t* Og = (uint16_t*)p.O + b * p.o_sb + hh * p.o_sh;

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
     }
   }
   if (row < p.n_q) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = row_sum_inverse(l, hi > lo);
 #pragma unroll
     for (int d = 0; d < DS; ++d) Og[(int64_t)row * p.o_sr + c0 + d] = o[d] * inv;
   }

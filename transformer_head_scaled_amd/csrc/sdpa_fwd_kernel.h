@@ -1002,8 +1002,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int qi = (SPLIT || PAIRS) ? 1 : 0; qi < QB; ++qi) {
     const float L = pair_sum(l[qi]);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
     const int row = row0[qi] + l32;
+    bool visible = n_eff > 0;  // (causal: key 0 is visible to every row)
+    if constexpr (WINDOW) visible = min(n_eff, row + p.win_right + 1) > max(0, row - p.win_left);
+    const float inv = row_sum_inverse(L, visible);
     if (wave_active && row < p.n_q) {
       uint16_t* orow = Og + (int64_t)row * p.o_sr;
 #pragma unroll

@@ -403,7 +403,7 @@ __global__ __launch_bounds__(256 * KS) void sdpa_wide_kernel(SdpaArgs p) {
 
   // normalise and store this wave's columns of the lane's row
   const float L = pair_sum(l);
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float inv = row_sum_inverse(L, n_eff > 0);
   const int row = row0 + l32;
   if (row < p.n_q) {
     uint16_t* orow = Og + (int64_t)row * p.o_sr + wave * DS;
