@@ -197,14 +197,14 @@ ALGORITHMIC = [
     ("cfg2", "mha_short_kernel<1, true, 4>",
      "base encoder Q/K/V projections + attention, one launch (x 2 MB, W^Q/K/V 3·0.5 MB, concat 2 MB)",
      2097152 + 3 * 524288 + 2097152),
-    ("cfg2", "gemm_kernel<1, 64, 64, 32, 32, 2>", "base encoder W^O (concat 2 MB, W 0.5 MB, out 2 MB)",
+    ("cfg2", "gemm_kernel<1, 64, 64, 32, 32, 2, 128>", "base encoder W^O (concat 2 MB, W 0.5 MB, out 2 MB)",
      2 * 2097152 + 524288),
     ("cfg4", "sdpa_fwd_kernel<1, 64, false, 8, false, false, true>", "[8,16,384→512,64]",
      2 * (2 * 8 * 16 * 384 * 64 + 2 * 8 * 16 * 512 * 64)),
-    ("cfg4", "gemm_kernel<1, 128, 128, 64, 64, 2>",
+    ("cfg4", "gemm_kernel<1, 128, 128, 64, 64, 2, 32>",
      "big cross-attention Q/K/V projections (x_q, x_kv, 3 W, Q/K/V out)",
      2 * (3072 * 1024 + 4096 * 1024 + 3 * 1024 * 1024 + 3072 * 1024 + 2 * 4096 * 1024)),
-    ("cfg4", "gemm_kernel<1, 64, 64, 32, 32, 2>", "big cross-attention W^O (concat, W, out)",
+    ("cfg4", "gemm_kernel<1, 64, 64, 32, 32, 2, 64>", "big cross-attention W^O (concat, W, out)",
      2 * (3072 * 1024 + 1024 * 1024 + 3072 * 1024)),
 ]
 
