@@ -17,6 +17,11 @@
  * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *   stream).  A status of MHA_OK means the work was validated and enqueued;
  *   faults inside a kernel surface at the caller's next synchronisation.
+ * - A call only enqueues kernels on `stream`: no synchronisation, no copy
+ *   and no memset.  Unless noted, a call also allocates nothing, so it can
+ *   be captured into a HIP graph.  The exceptions are mha_forward and
+ *   mha_forward_add_norm given no workspace: they allocate stream-ordered.
+ *   Each replay writes what the eager call writes, bit for bit.
  * - Every argument is validated on the host before anything is enqueued, so
  *   an error return never leaves partial output.  Device-side key lengths
  *   cannot be read without a synchronisation; the kernels clamp each one to
