@@ -63,6 +63,23 @@ def test_workload_causal_b16_n512(dtype):
     _check(got, exp, dtype, f"{dtype} causal [16,8,512,64]")
 
 
+def test_causal_resident_grid_second_round_order():
+    """Causal [8,8,600,64]: 320 four-wave pair workgroups, all resident at
+    once, whose second-round slots take the row groups shortest first.  Rows
+    are ragged (600 = 4·128 + 88) and so are the key lengths; every output
+    against the oracle, then bitwise against the opposite launch order."""
+    B, h, n = 8, 8, 600
+    r = libmha.sdpa_route(libmha.MHA_BF16, B, h, n, n, 64, mask="causal")
+    assert (r["kernel"], r["waves"], r["workgroups"]) == ("pairs", 4, 320), r
+    ins = synth.sdpa_inputs(14, B, h, n, n, 64, dtype="bf16")
+    lens = np.random.default_rng(14).integers(250, n + 1, size=B).astype(np.int32)
+    lens[0] = n
+    note(f"sdpa bf16 causal [8,8,600,64] lens {lens.tolist()}")
+    got = _run(ins, "bf16", "causal", lens=lens)
+    exp = oracle.sdpa(ins["Q"][1], ins["K"][1], ins["V"][1], 0.125, oracle.MASK_CAUSAL, lens)
+    _check(got, exp, "bf16", "causal [8,8,600,64] ragged lens")
+
+
 @pytest.mark.parametrize("mask", ["none", "causal"])
 def test_workload_long_b4_n4096_all_heads(mask):
     """[4,8,4096,64], the launch the bench times: every output of every one
@@ -694,6 +711,7 @@ def test_repeatable_bitwise():
 @pytest.mark.parametrize("shape,mask", [
     ((8, 8, 2048, 64), "none"),      # two-block layout, eight waves
     ((2, 8, 2048, 64), "causal"),    # pair layout
+    ((8, 8, 600, 64), "causal"),     # pair layout, second round shortest first
     ((4, 4, 640, 64), "none"),       # unmasked pair layout
     ((3, 2, 1000, 32), "causal"),    # two-block causal layout (blocks u, nb - 1 - u)
     ((8, 4, 3, 1500, 64), "none"),   # key split (n_q 3 against 1500 keys)

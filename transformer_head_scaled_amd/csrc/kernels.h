@@ -28,6 +28,10 @@ struct SdpaArgs {
   // launch the workgroups in the opposite order (the flash kernel; the
   // results are the same, which the determinism tests check)
   int32_t reverse;
+  // pair layout, whole grid resident at once: the first slot of each XCD's
+  // second round (the row groups there run shortest first); 0: longest
+  // first throughout
+  int32_t pair_split;
 };
 
 // The attention kernel a problem runs on, and its workgroup shape

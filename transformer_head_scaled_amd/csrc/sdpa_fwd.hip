@@ -137,11 +137,20 @@ hipError_t launch_nw(const SdpaArgs& a, hipStream_t st) {
 }
 
 // the pair layout: a workgroup of NW waves takes NW consecutive 32-row blocks
+// Causal, d = 64, at most four waves: 64 KB of LDS and at most two waves a
+// SIMD, so two workgroups share a CU; a grid of at most 512 (and more than
+// 256) workgroups is resident at once, workgroup x beside x + 256 (the
+// dispatcher deals them round-robin to the 8 XCDs and within an XCD to its
+// 32 CUs in turn).  The row groups of the second round then run shortest
+// first (pair_split, the kernel): [16,8,512,64] pairs row groups 3 and 0,
+// 2 and 1 on a CU instead of 3 and 1, 2 and 0.
 template <int DT, int DH, bool CAUSAL, int NW>
 hipError_t launch_pairs_nw(const SdpaArgs& a, hipStream_t st) {
   const int64_t grid = (a.n_q + NW * 32 - 1) / (NW * 32) * a.B * a.H;
+  SdpaArgs b = a;
+  b.pair_split = (CAUSAL && DH == 64 && NW <= 4 && (a.B * a.H) % 8 == 0 && grid > 256 && grid <= 512) ? 32 : 0;
   hipLaunchKernelGGL((sdpa_fwd_kernel<DT, DH, CAUSAL, NW, false, false, true>), dim3((unsigned)grid),
-                     dim3(NW * 64), 0, st, a);
+                     dim3(NW * 64), 0, st, b);
   return hipGetLastError();
 }
 

@@ -182,12 +182,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   // them row group by row group from the top, so a head's K/V is read from
   // memory by one XCD (round-robin heads measured as fast but re-read them:
   // 79 MB against 67 MB per launch); otherwise consecutive workgroups are
-  // different heads at the same rows.
+  // different heads at the same rows.  When the whole grid is resident at
+  // once (pair_split != 0: two workgroups a CU, x and x + 8·pair_split on
+  // one CU), the second round's slots of each XCD take the row groups in
+  // the opposite order, shortest first, so that a CU holds a long and a
+  // short row group instead of two of the same rank.
   const uint32_t hw = p.reverse ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
   const uint32_t t = PAIRS ? hw : xcd_remap(hw, total);
   const uint32_t nbh = (uint32_t)p.B * p.H;
   const bool xcd_heads = PAIRS && nbh % 8 == 0;
-  const uint32_t hpx = nbh / 8, xk = t / 8;
+  const uint32_t hpx = nbh / 8, ps = (uint32_t)p.pair_split;
+  const uint32_t xk = (PAIRS && ps != 0 && t / 8 >= ps) ? ps + (total / 8 - 1 - t / 8) : t / 8;
   const int bh = !PAIRS ? (int)(t / nqb)
                  : xcd_heads ? (int)((t % 8) * hpx + xk % hpx) : (int)(t % nbh);
   const int qb = !PAIRS ? (int)(t % nqb)
