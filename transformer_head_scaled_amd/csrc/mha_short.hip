@@ -156,18 +156,27 @@ __global__ __launch_bounds__(256) void mha_short_kernel(ShortArgs a) {
     // stage (kt − 1) % NST was last read in step kt − 1, which every wave has left
     if (kt + NST - 1 < nk) gload(kt + NST - 1, (kt + NST - 1) % NST);
     if (mat < 3) {
+      // every fragment of the stage first, then its MFMAs (pinned by the
+      // schedule groups): with one wave a SIMD nothing else hides a read's
+      // latency, and the compiler would otherwise read each 16-k step's
+      // fragments just before their MFMAs (+2-3 % on the base encoder
+      // sub-layer, identical results)
+      u32x4 wf[SBK / 16][2], xf[SBK / 16][2];
 #pragma unroll
       for (int ks = 0; ks < SBK / 16; ++ks) {
-        u32x4 wf[2], xf[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) wf[i] = wfrag(buf, i, ks);
+        for (int i = 0; i < 2; ++i) wf[ks][i] = wfrag(buf, i, ks);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) xf[j] = xfrag(buf, j, ks);
+        for (int j = 0; j < 2; ++j) xf[ks][j] = xfrag(buf, j, ks);
+      }
+#pragma unroll
+      for (int ks = 0; ks < SBK / 16; ++ks)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16<DT>(wf[i], xf[j], acc[i][j]);
-      }
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16<DT>(wf[ks][i], xf[ks][j], acc[i][j]);
+      __builtin_amdgcn_sched_group_barrier(0x100, (SBK / 16) * 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, (SBK / 16) * 4, 0);
     }
     // stage kt + 1 landed, this stage's reads done
     wait_next(min(nk - 1, kt + NST - 1) - (kt + 1));
