@@ -491,6 +491,33 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
     }
     return rs0 + rs1;
   };
+  // A row block's first tile with a visible key: the accept test cannot
+  // pass against a reference value of −∞, so the reference becomes the
+  // tile's row max, taken from the scores in registers before the weights
+  // are formed -- what the exact path below would set, without recomputing
+  // the scores twice from LDS (o and l are still 0, so nothing is
+  // rescaled; the results are bit-identical).  Rows that see no key here
+  // keep −∞ and still take the exact path.  Only where a row block sees
+  // few tiles, so that its first one weighs: the window (reach 0 +27 %,
+  // 256 +13 %), the key split (+4 %) and d <= 32 (causal d 32 +3 %).  In the
+  // d 64 and 128 kernels the test in the loop cost more than it saved
+  // (unmasked [4,8,4096,64] −1.7 %, d 128 −7.5 %).
+  constexpr bool kFirstRef = WINDOW || SPLIT || DH <= 32;
+  auto first_ref = [&](int qi, const f32x16 (&sv)[2]) __attribute__((always_inline)) {
+    if (!kFirstRef) return;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(m[qi] == -INFINITY) != 0, 0)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kb][i]);
+      mx = pair_max(mx);
+      if (m[qi] == -INFINITY) {
+        m[qi] = mx;
+        mc[qi] = (mx == -INFINITY ? 0.f : mx) * c;
+      }
+    }
+  };
   // per-element mask of query block qi (diagonal and key-length boundary
   // tiles only)
   auto apply_mask = [&](int qi, int kbase, int kb, f32x16& sv) __attribute__((always_inline)) {
@@ -589,6 +616,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
       apply_mask(0, kbase, 1, s0[1]);
     }
     uint32_t p0[2][8], p1[2][8];
+    first_ref(0, s0);
     const float rs0 = weights(0, 0, s0[0], p0[0]) + weights(0, 1, s0[1], p0[1]);
     // (vector work first, then one MFMA: measured 0.6-1 % faster at d 64
     // and 3 % at d 128 than MFMA first; in the pair tile code below the
@@ -633,6 +661,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
       apply_mask(1, kbase, 0, s1[0]);
       apply_mask(1, kbase, 1, s1[1]);
     }
+    first_ref(1, s1);
     const float rs1 = weights(1, 0, s1[0], p1[0]) + weights(1, 1, s1[1], p1[1]);
 #pragma unroll
     for (int g = 0; g < 4 * NDB; ++g) {
@@ -675,6 +704,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
       apply_mask(1, kbase, 1, s1[1]);
     }
     uint32_t p1[2][8];
+    first_ref(1, s1);
     const float rs1 = weights(1, 0, s1[0], p1[0]) + weights(1, 1, s1[1], p1[1]);
     settle(masked, 1, buf, kbase, p1, rs1);
     constexpr bool CHECK_V = MASKED && (CAUSAL || WINDOW);
@@ -736,6 +766,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
       apply_mask(1, kbaseA, 1, sa[1]);
     }
     uint32_t pa[2][8], pb[2][8];
+    first_ref(1, sa);
     const float rsa = weights(1, 0, sa[0], pa[0]) + weights(1, 1, sa[1], pa[1]);
 #pragma unroll
     for (int g = 0; g < 2 * NST; ++g) {
@@ -773,6 +804,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
       apply_mask(1, kbaseB, 0, sb[0]);
       apply_mask(1, kbaseB, 1, sb[1]);
     }
+    first_ref(1, sb);
     const float rsb = weights(1, 0, sb[0], pb[0]) + weights(1, 1, sb[1], pb[1]);
 #pragma unroll
     for (int g = 0; g < 4 * NDB; ++g) {
