@@ -503,20 +503,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   // d 64 and 128 kernels the test in the loop cost more than it saved
   // (unmasked [4,8,4096,64] −1.7 %, d 128 −7.5 %).
   constexpr bool kFirstRef = WINDOW || SPLIT || DH <= 32;
+  auto set_ref = [&](int qi, const f32x16 (&sv)[2]) __attribute__((always_inline)) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kb][i]);
+    mx = pair_max(mx);
+    if (m[qi] == -INFINITY) {
+      m[qi] = mx;
+      mc[qi] = (mx == -INFINITY ? 0.f : mx) * c;
+    }
+  };
   auto first_ref = [&](int qi, const f32x16 (&sv)[2]) __attribute__((always_inline)) {
     if (!kFirstRef) return;
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(m[qi] == -INFINITY) != 0, 0)) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kb][i]);
-      mx = pair_max(mx);
-      if (m[qi] == -INFINITY) {
-        m[qi] = mx;
-        mc[qi] = (mx == -INFINITY ? 0.f : mx) * c;
-      }
-    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(m[qi] == -INFINITY) != 0, 0)) set_ref(qi, sv);
   };
   // per-element mask of query block qi (diagonal and key-length boundary
   // tiles only)
@@ -893,6 +894,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   // takes part in all ntiles barriers.
   using no = std::false_type;
   using yes = std::true_type;
+  // The kernels without first_ref (d 64 and 128, no window, no key split)
+  // take the first tile's row max once, before the key loop: its scores
+  // (masked, which is exact for any tile) from LDS stage 0, where the
+  // prologue has put the workgroup's first tile.  The loop's first tile then
+  // passes the accept test with the same weights the exact path would form,
+  // for 8 MFMAs a block instead of that path's 16 (bit-identical results),
+  // and the loop itself is unchanged.
+  if constexpr (!kFirstRef) {
+    if (jlo < ntiles) {
+#pragma unroll
+      for (int qi = PAIRS ? 1 : 0; qi < QB; ++qi) {
+        f32x16 sv[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sv[kb] = scores(yes{}, qi, 0, jlo * BN, kb);
+        set_ref(qi, sv);
+      }
+    }
+  }
   const int nfull = min(n_eff / BN, ntiles);  // tiles inside the valid keys
   int j = jlo;
   if (PAIRS) {
