@@ -192,7 +192,7 @@ ROUTES = [
     ((M.MHA_BF16, 4, 2, 4, 1000, 128, "none", None), ("split", 2, None)),
     ((M.MHA_BF16, 1, 2, 200, 200, 32, "causal", None), ("blocks", 2, None)),
     ((M.MHA_BF16, 1, 2, 200, 200, 512, "causal", None), ("wide", 8, 14)),  # key tiles split in two
-    ((M.MHA_BF16, 1, 2, 200, 200, 512, "none", None), ("wide", 4, 14)),
+    ((M.MHA_BF16, 1, 2, 200, 200, 512, "none", None), ("wide", 8, 8)),   # two 32-row blocks a workgroup
     ((M.MHA_BF16, 1, 2, 200, 200, 256, "causal", None), ("wide", 4, 14)),
     ((M.MHA_BF16, 8, 16, 1000, 1000, 64, "none", (128, 128)), ("window", 2, None)),
     ((M.MHA_BF16, 8, 16, 2600, 2600, 64, "none", (1500, 600)), ("window", 4, None)),

@@ -327,6 +327,7 @@ WIDE_CASES = [
     (3, 2, 50, 97, "none", [97, 31, 0]),
     (1, 1, 257, 257, "causal", [200]),
     (2, 1, 33, 600, "none", None),
+    (2, 2, 300, 300, "none", [300, 129]),   # unmasked: five 64-row workgroups, the last ragged
 ]
 
 

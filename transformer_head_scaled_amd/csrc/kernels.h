@@ -62,8 +62,10 @@ hipError_t launch_sdpa(const SdpaArgs& a, const SdpaRoute& r, int dtype, int cau
 // the flash kernel's window form (bf16 / fp16), sdpa_window.hip
 hipError_t launch_sdpa_window(const SdpaArgs& a, const SdpaRoute& r, int dtype, int d, hipStream_t st);
 // wide heads, d = 256 or 512 (bf16 / fp16, no window), sdpa_wide.hip; 8
-// waves: causal with the key tiles split between two groups of 4
-hipError_t launch_sdpa_wide(const SdpaArgs& a, int dtype, int causal, int d, int waves, hipStream_t st);
+// waves: 32 rows (causal, the key tiles split between two groups of 4) or
+// 64 rows (two 32-row blocks sharing the staged tiles)
+hipError_t launch_sdpa_wide(const SdpaArgs& a, int dtype, int causal, int d, int waves, int rows,
+                            hipStream_t st);
 // the smallest head dimension whose causal form splits the key tiles
 #ifndef SDPA_WIDE_SPLIT_MIN_D
 #define SDPA_WIDE_SPLIT_MIN_D 512

@@ -235,7 +235,7 @@ hipError_t launch_sdpa(const SdpaArgs& a, const SdpaRoute& r, int dtype, int cau
         case 128: return launch_f32<128>(a, r, scale, causal, st);
       }
       break;
-    case SDPA_K_WIDE: return launch_sdpa_wide(a, dtype, causal, d, r.waves, st);
+    case SDPA_K_WIDE: return launch_sdpa_wide(a, dtype, causal, d, r.waves, r.rows, st);
     case SDPA_K_WINDOW: return launch_sdpa_window(a, r, dtype, d, st);
     case SDPA_K_DECODE:
       if (causal || a.window) break;

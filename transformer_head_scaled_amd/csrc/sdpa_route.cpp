@@ -9,8 +9,9 @@
 // the alternatives on one box, identical results):
 //
 // * fp32: one kernel, 64 rows a workgroup.
-// * d = 256, 512: the wide-head kernel, one 32-row block per workgroup of 4
-//   waves that split d.
+// * d = 256, 512: the wide-head kernel, 4 waves that split d per 32-row
+//   block: unmasked, two blocks a workgroup sharing the staged K/V tiles;
+//   causal, one block (at d = 512 with the key tiles split in two groups).
 // * A window: the flash kernel's window form, rows as in the unmasked
 //   two-block layout, at most 2 waves a workgroup while the window spans
 //   fewer than 2048 keys besides the row itself (a workgroup walks the key
@@ -111,7 +112,12 @@ SdpaRoute sdpa_route(int dtype, bool causal, bool window, int64_t B, int64_t H, 
   } else if (d > 128) {
     // causal, wide enough: the key tiles split between two groups (the
     // merge costs more than the split gains at d = 256)
-    r.kernel = SDPA_K_WIDE, r.waves = (causal && d >= SDPA_WIDE_SPLIT_MIN_D) ? 8 : 4, r.rows = 32;
+    // causal at d = 512: the key tiles split between two groups; unmasked:
+    // two 32-row blocks a workgroup sharing each staged tile (d 256 +22 %,
+    // 512 +8 %; causal d 256 lost 11 %, its longest row block growing)
+    const bool ksplit = causal && d >= SDPA_WIDE_SPLIT_MIN_D;
+    const int rs = causal ? 1 : 2;
+    r.kernel = SDPA_K_WIDE, r.waves = ksplit ? 8 : 4 * rs, r.rows = 32 * rs;
   } else if (window) {
     int w = blocks_waves(n_q, heads);
     if (w > 2 && win_left + win_right < 2048) w = 2;

@@ -39,9 +39,13 @@ namespace {
 
 // KS key groups of NW waves: KS = 2 splits a block's key tiles between two
 // groups (even and odd tiles), each with its own LDS buffers, and merges the
-// two partial results at the end.
-template <int DT, int D, bool CAUSAL, int KS = 1>
-__global__ __launch_bounds__(256 * KS) void sdpa_wide_kernel(SdpaArgs p) {
+// two partial results at the end.  RS row groups: RS = 2 gives the
+// workgroup two consecutive 32-row blocks, one per group of NW waves, which
+// share every staged K and V tile (half the tile bytes per flop) and keep
+// their own score exchange; both groups walk the same tiles and barriers.
+template <int DT, int D, bool CAUSAL, int KS = 1, int RS = 1>
+__global__ __launch_bounds__(256 * KS * RS) void sdpa_wide_kernel(SdpaArgs p) {
+  static_assert(KS == 1 || RS == 1, "a key split or a row split, not both");
   constexpr int NW = 4, BN = 32;
   constexpr int DS = D / NW;         // columns per wave
   constexpr int NST = DS / 16;       // 16-deep MFMA steps of a partial score block
@@ -57,10 +61,10 @@ __global__ __launch_bounds__(256 * KS) void sdpa_wide_kernel(SdpaArgs p) {
   // partial scores: lane l's 16 values as four 16-byte chunks, chunk c
   // stored at c ^ ((l >> 2) & 3) (the 16 lanes of a 16-byte access phase
   // then cover all 64 banks)
-  __shared__ __attribute__((aligned(16))) float Sx[KS][NW][64 * 16];
+  __shared__ __attribute__((aligned(16))) float Sx[KS * RS][NW][64 * 16];
   constexpr float kAccept = 256.f;
 
-  const int nqb = (p.n_q + 31) / 32;
+  const int nqb = (p.n_q + 32 * RS - 1) / (32 * RS);
   const uint32_t nbh = (uint32_t)p.B * p.H;
   // causal: the highest blocks (most keys) first
   const int qb = CAUSAL ? nqb - 1 - (int)(blockIdx.x / nbh) : (int)(blockIdx.x / nbh);
@@ -69,15 +73,21 @@ __global__ __launch_bounds__(256 * KS) void sdpa_wide_kernel(SdpaArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   // (the wave index within its key group: it selects the columns)
   const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = KS == 1 ? 0 : wave_all / NW, wave = KS == 1 ? wave_all : wave_all % NW;
+  const int grp = (KS == 1 && RS == 1) ? 0 : wave_all / NW;
+  const int wave = (KS == 1 && RS == 1) ? wave_all : wave_all % NW;
+  const int kvg = KS == 1 ? 0 : grp;  // this wave's K and V buffers
   const int l32 = lane & 31, hi = lane >> 5;
-  const int row0 = qb * 32;
+  const int row0 = qb * 32 * RS + (RS == 1 ? 0 : 32 * grp);
 
   int n_eff = p.n_k;
   if (p.lens) n_eff = min(max(p.lens[b], 0), p.n_k);
   int kend = n_eff;
   if (CAUSAL) kend = min(kend, row0 + 32);
-  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;  // this block's tiles
+  // the workgroup's tiles (its highest block's, with the row split)
+  int kend_wg = n_eff;
+  if (CAUSAL) kend_wg = min(kend_wg, qb * 32 * RS + 32 * RS);
+  const int ntiles_wg = RS == 1 ? ntiles : (kend_wg > 0 ? (kend_wg + BN - 1) / BN : 0);
 
   const uint16_t* Qg = (const uint16_t*)p.Q + b * p.q_sb + hh * p.q_sh;
   const uint16_t* Kg = (const uint16_t*)p.K + b * p.k_sb + hh * p.k_sh;
@@ -122,7 +132,9 @@ __global__ __launch_bounds__(256 * KS) void sdpa_wide_kernel(SdpaArgs p) {
   // wave instruction fills 1 KB: lane i writes chunk position i of a row
   // (d = 512) or of one of two rows (d = 256).
   constexpr int PIECES = BN * D * 2 / 1024;  // 1 KB pieces per tile
-  constexpr int CPW = PIECES / NW;
+  constexpr int CPW = PIECES / (NW * RS);  // pieces per wave and tile
+  static_assert(PIECES % (NW * RS) == 0, "tile pieces per wave");
+  const int lw = RS == 1 ? wave : wave_all;  // this wave's share of the loads
   auto piece_src = [&](int r, bool is_v) __attribute__((always_inline)) {
     const int key = (PPR >= 1) ? r : 2 * r + lane / CR;  // PPR >= 1: one row per piece
     const int pos = lane % CR;
@@ -132,27 +144,27 @@ __global__ __launch_bounds__(256 * KS) void sdpa_wide_kernel(SdpaArgs p) {
   auto gload_k = [&](int tile) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
-      const int r = wave * CPW + i;
+      const int r = lw * CPW + i;
       load_lds_b128(krs,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-                        __attribute__((address_space(3))) void*)&Ks[grp][r * 512]),
+                        __attribute__((address_space(3))) void*)&Ks[kvg][r * 512]),
                     piece_src(r, false) + (uint32_t)(tile * BN * p.k_sr * 2));
     }
   };
   auto gload_v = [&](int tile) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
-      const int r = wave * CPW + i;
+      const int r = lw * CPW + i;
       load_lds_b128(vrs,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-                        __attribute__((address_space(3))) void*)&Vs[grp][r * 512]),
+                        __attribute__((address_space(3))) void*)&Vs[kvg][r * 512]),
                     piece_src(r, true) + (uint32_t)(tile * BN * p.v_sr * 2));
     }
   };
   // K fragment st of this wave: key l32, chunk (wave·DS)/8 + 2·st + hi
   auto kfrag = [&](int st) __attribute__((always_inline)) {
     const int ch = (wave * DS) / 8 + 2 * st + hi;
-    return *(const u32x4*)&Ks[grp][l32 * D + ((ch ^ (l32 & 15)) * 8)];
+    return *(const u32x4*)&Ks[kvg][l32 * D + ((ch ^ (l32 & 15)) * 8)];
   };
   // Vᵀ fragment (t2, db): d = wave·DS + db·32 + l32, keys of the 16-key step
   // t2 in the score-register order, two transposing reads of 4 keys
@@ -166,7 +178,7 @@ __global__ __launch_bounds__(256 * KS) void sdpa_wide_kernel(SdpaArgs p) {
       const int key = t2 * 16 + 8 * e + v_key_l;
       const int d = wave * DS + db * 32 + v_col;
       const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)&Vs[grp][key * D + (((d >> 3) ^ (4 * (key & 3))) * 8) + (d & 7)]);
+          (lds_s16x4*)&Vs[kvg][key * D + (((d >> 3) ^ (4 * (key & 3))) * 8) + (d & 7)]);
       const u32x2 w = __builtin_bit_cast(u32x2, v);
       r[2 * e] = w[0];
       r[2 * e + 1] = w[1];
@@ -261,7 +273,7 @@ __global__ __launch_bounds__(256 * KS) void sdpa_wide_kernel(SdpaArgs p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d = wave * DS + db * 32 + 8 * g + 4 * hi;
-          const u32x2 w = *(const u32x2*)&Vs[grp][k * D + (((d >> 3) ^ (4 * (k & 3))) * 8) + (d & 7)];
+          const u32x2 w = *(const u32x2*)&Vs[kvg][k * D + (((d >> 3) ^ (4 * (k & 3))) * 8) + (d & 7)];
           const f32x4 x = unpack4<DT>(w);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -318,21 +330,22 @@ __global__ __launch_bounds__(256 * KS) void sdpa_wide_kernel(SdpaArgs p) {
   // group grp takes the tiles grp, grp + KS, ...; both groups run the same
   // number of steps (two workgroup barriers each), a group past its last
   // tile only taking part in the barriers
-  const int niter = (ntiles + KS - 1) / KS;
-  if (grp < ntiles) {
-    gload_k(grp);
-    gload_v(grp);
+  const int niter = (ntiles_wg + KS - 1) / KS;
+  const int j0 = KS == 1 ? 0 : grp;  // the first tile of this wave's key group
+  if (j0 < ntiles_wg) {
+    gload_k(j0);
+    gload_v(j0);
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   asm volatile("s_barrier" ::: "memory");
   for (int it = 0; it < niter; ++it) {
-    const int j = grp + KS * it;
-    const bool mine = KS == 1 || j < ntiles;
+    const int j = j0 + KS * it;
+    const bool mine = j < ntiles;
     if (mine) put_sx(spart());
     // exchange writes visible, V(j) landed, every wave past its K reads
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-    if (j + KS < ntiles) gload_k(j + KS);
+    if (j + KS < ntiles_wg) gload_k(j + KS);
     if (mine) {
       f32x16 s = get_sx();
       uint32_t pw[8];
@@ -342,7 +355,7 @@ __global__ __launch_bounds__(256 * KS) void sdpa_wide_kernel(SdpaArgs p) {
     // K(j + KS) landed, every wave past its V and exchange reads
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-    if (j + KS < ntiles) gload_v(j + KS);
+    if (j + KS < ntiles_wg) gload_v(j + KS);
   }
 
   if constexpr (KS == 2) {
@@ -420,8 +433,16 @@ __global__ __launch_bounds__(256 * KS) void sdpa_wide_kernel(SdpaArgs p) {
 }
 
 template <int DT, int D>
-hipError_t launch_d(const SdpaArgs& a, int causal, int waves, hipStream_t st) {
-  const int64_t grid = (a.n_q + 31) / 32 * (int64_t)a.B * a.H;
+hipError_t launch_d(const SdpaArgs& a, int causal, int waves, int rows, hipStream_t st) {
+  const int64_t grid = (a.n_q + rows - 1) / rows * (int64_t)a.B * a.H;
+  if (rows == 64 && waves == 8) {  // the row split
+    if (causal)
+      hipLaunchKernelGGL((sdpa_wide_kernel<DT, D, true, 1, 2>), dim3((unsigned)grid), dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((sdpa_wide_kernel<DT, D, false, 1, 2>), dim3((unsigned)grid), dim3(512), 0, st, a);
+    return hipGetLastError();
+  }
+  if (rows != 32) return hipErrorInvalidValue;
   if constexpr (D >= SDPA_WIDE_SPLIT_MIN_D) {
     if (causal && waves == 8) {
       hipLaunchKernelGGL((sdpa_wide_kernel<DT, D, true, 2>), dim3((unsigned)grid), dim3(512), 0, st, a);
@@ -439,14 +460,15 @@ hipError_t launch_d(const SdpaArgs& a, int causal, int waves, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_sdpa_wide(const SdpaArgs& a, int dtype, int causal, int d, int waves, hipStream_t st) {
+hipError_t launch_sdpa_wide(const SdpaArgs& a, int dtype, int causal, int d, int waves, int rows,
+                            hipStream_t st) {
   if (a.window) return hipErrorInvalidValue;  // not offered for wide heads
   if (dtype == DT_BF16) {
-    if (d == 256) return launch_d<DT_BF16, 256>(a, causal, waves, st);
-    if (d == 512) return launch_d<DT_BF16, 512>(a, causal, waves, st);
+    if (d == 256) return launch_d<DT_BF16, 256>(a, causal, waves, rows, st);
+    if (d == 512) return launch_d<DT_BF16, 512>(a, causal, waves, rows, st);
   } else if (dtype == DT_F16) {
-    if (d == 256) return launch_d<DT_F16, 256>(a, causal, waves, st);
-    if (d == 512) return launch_d<DT_F16, 512>(a, causal, waves, st);
+    if (d == 256) return launch_d<DT_F16, 256>(a, causal, waves, rows, st);
+    if (d == 512) return launch_d<DT_F16, 512>(a, causal, waves, rows, st);
   }
   return hipErrorInvalidValue;
 }
