@@ -3,8 +3,11 @@
 // §3.2.1, for the head sizes of its Table 3 row (A) with few heads
 // (d_model 512 with h = 1 gives d_k = d_v = 512).
 //
-// One 32-row query block per workgroup of 4 waves, the head dimension split
+// One 32-row query block per group of 4 waves, the head dimension split
 // across the waves: wave w owns columns [w·D/4, (w+1)·D/4) of Q, K, V and O.
+// Unmasked, a workgroup holds two such groups on consecutive blocks, which
+// share every staged K/V tile (RS = 2); causal at d = 512, two groups
+// share one block and split its key tiles (KS = 2).
 // The output accumulator of a block at d = 512 would need 256 registers
 // per lane in one wave; split four ways it needs 64.  The scores need the
 // whole contraction over d, so per 32-key tile each wave forms the partial
