@@ -438,11 +438,9 @@ __global__ __launch_bounds__(256 * KS * RS) void sdpa_wide_kernel(SdpaArgs p) {
 template <int DT, int D>
 hipError_t launch_d(const SdpaArgs& a, int causal, int waves, int rows, hipStream_t st) {
   const int64_t grid = (a.n_q + rows - 1) / rows * (int64_t)a.B * a.H;
-  if (rows == 64 && waves == 8) {  // the row split
-    if (causal)
-      hipLaunchKernelGGL((sdpa_wide_kernel<DT, D, true, 1, 2>), dim3((unsigned)grid), dim3(512), 0, st, a);
-    else
-      hipLaunchKernelGGL((sdpa_wide_kernel<DT, D, false, 1, 2>), dim3((unsigned)grid), dim3(512), 0, st, a);
+  if (rows == 64) {  // the row split, unmasked only (the route's choice)
+    if (causal || waves != 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((sdpa_wide_kernel<DT, D, false, 1, 2>), dim3((unsigned)grid), dim3(512), 0, st, a);
     return hipGetLastError();
   }
   if (rows != 32) return hipErrorInvalidValue;
