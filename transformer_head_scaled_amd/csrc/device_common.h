@@ -106,6 +106,24 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
 
+// Output stores of a 32x32 MFMA result held one row per lane pair: lanes
+// l and l + 32 hold the same row, lane hi = 0 columns 0..3 and 8..11 of a
+// 16-column group, lane hi = 1 columns 4..7 and 12..15 (each 4-column
+// piece as two packed pairs: a = the piece at 4·hi, b = the one at
+// 8 + 4·hi).  Swapping one piece with the partner gives lane hi = 0
+// columns 0..7 and lane hi = 1 columns 8..15: one 16-byte store per lane
+// at column 8·hi instead of two of 8 bytes.  Both lanes of a pair must be
+// active.
+__device__ __forceinline__ u32x4 row_pair_pieces(u32x2 a, u32x2 b, int hi) {
+  const u32x2 send = hi ? a : b;
+  const auto r0 = __builtin_amdgcn_permlane32_swap(send[0], send[0], false, false);
+  const auto r1 = __builtin_amdgcn_permlane32_swap(send[1], send[1], false, false);
+  // lanes 0..31 find the partner's value in the second result, 32..63 in the first
+  const uint32_t q0 = hi ? (uint32_t)r0[0] : (uint32_t)r0[1];
+  const uint32_t q1 = hi ? (uint32_t)r1[0] : (uint32_t)r1[1];
+  return hi ? u32x4{q0, q1, b[0], b[1]} : u32x4{a[0], a[1], q0, q1};
+}
+
 // 1 / (a row's weight sum), for the normalisation.  A sum of 0 means no
 // visible key (the row's output is 0) or, with visible keys, only scores of
 // −∞ among them -- infinite inputs; the exact softmax is then 0/0, NaN.  (A

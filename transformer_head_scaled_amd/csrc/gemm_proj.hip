@@ -13,8 +13,9 @@
 // Cᵀ = Wᵀ·Aᵀ with the 32x32x16 MFMA: the B operand (Aᵀ) is a 16-byte read
 // of an A row, the A operand (Wᵀ) comes from transposing LDS reads
 // (ds_read_b64_tr_b16) of the row-major W tile.  In the Cᵀ result a lane
-// holds 4 consecutive n of one row m, written as one 8-byte store, and the
-// head split / concat is folded into the store address (see GemmProblem).
+// holds 4 consecutive n of one row m; the two lanes of a row exchange
+// pieces so that each writes 8 consecutive n with one 16-byte store, and
+// the head split / concat is folded into the store address (GemmProblem).
 //
 // Tiles: TM × TN outputs per workgroup of 4 waves (2 × 2, each TM/2 × TN/2),
 // two LDS stages of 64 k (64 × 64 tiles; 128 k for grids of at most two
@@ -253,7 +254,7 @@ __global__ __launch_bounds__((TM / WTM) * (TN / WTN) * 64) void gemm_kernel(Gemm
 #pragma unroll
   for (int i = 0; i < WN; ++i) {
     const int nb = n0 + wn * WTN + i * 32;
-    col_off[i] = (int64_t)(nb / P.head_dim) * P.c_sh + nb % P.head_dim + hi * 4;
+    col_off[i] = (int64_t)(nb / P.head_dim) * P.c_sh + nb % P.head_dim;
   }
   const int64_t half_step = P.head_dim == 16 ? P.c_sh : 16;  // offset of columns 16..31
   uint16_t* Cg = (uint16_t*)P.C;
@@ -266,10 +267,17 @@ __global__ __launch_bounds__((TM / WTM) * (TN / WTN) * 64) void gemm_kernel(Gemm
 #pragma unroll
     for (int i = 0; i < WN; ++i)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const u32x2 w = {pack2<DT>(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]),
-                         pack2<DT>(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3])};
-        *(u32x2*)(crow + col_off[i] + (gq >> 1) * half_step + (gq & 1) * 8) = w;
+      for (int gp = 0; gp < 2; ++gp) {
+        const int ga = 2 * gp, gb = 2 * gp + 1;
+        const u32x2 wa = {pack2<DT>(acc[i][j][4 * ga], acc[i][j][4 * ga + 1]),
+                          pack2<DT>(acc[i][j][4 * ga + 2], acc[i][j][4 * ga + 3])};
+        const u32x2 wb = {pack2<DT>(acc[i][j][4 * gb], acc[i][j][4 * gb + 1]),
+                          pack2<DT>(acc[i][j][4 * gb + 2], acc[i][j][4 * gb + 3])};
+        // one 16-byte store per lane (the stores of every tile go out
+        // together at the end; half as many requests measured the big
+        // cross-attention sub-layer 7.9 % faster)
+        const u32x4 w = row_pair_pieces(wa, wb, hi);
+        *(u32x4*)(crow + col_off[i] + gp * half_step + 8 * hi) = w;
       }
   }
 }

@@ -426,11 +426,15 @@ __global__ __launch_bounds__(256 * KS * RS) void sdpa_wide_kernel(SdpaArgs p) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + g * 8 + hi * 4;
-        const u32x2 w = {pack2<DT>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                         pack2<DT>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-        *(u32x2*)(orow + d) = w;
+      for (int gp = 0; gp < 2; ++gp) {
+        u32x2 w[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int g = 2 * gp + e;
+          w[e] = u32x2{pack2<DT>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                       pack2<DT>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+        }
+        *(u32x4*)(orow + db * 32 + gp * 16 + 8 * hi) = row_pair_pieces(w[0], w[1], hi);
       }
   }
 }
