@@ -57,24 +57,34 @@ __global__ __launch_bounds__(64) void sdpa_f32_kernel(SdpaArgs p, float scale, i
     hi = min(hi, row + p.win_right + 1);
   }
 
+  // (one test for the whole row, so that the loads go out together rather
+  // than one branch and one wait per element)
   float q[DS], o[DS];
 #pragma unroll
-  for (int d = 0; d < DS; ++d) {
-    q[d] = row < p.n_q ? Qg[(int64_t)row * p.q_sr + c0 + d] : 0.f;
-    o[d] = 0.f;
+  for (int d = 0; d < DS; ++d) q[d] = o[d] = 0.f;
+  if (row < p.n_q) {
+#pragma unroll
+    for (int d = 0; d < DS; ++d) q[d] = Qg[(int64_t)row * p.q_sr + c0 + d];
   }
   double m = -INFINITY;
   float l = 0.f;
 
   for (int j = jlo; j < ntiles; ++j) {
     __syncthreads();
-    for (int e = threadIdx.x; e < TK * DH / 4; e += 64) {
+    // a fixed trip count, and keys past the valid length read from the last
+    // valid key and then cleared (no branch around the loads), so that the
+    // loads of a thread can all be in flight together (n_eff >= 1 here: a
+    // tile exists only below kend <= n_eff)
+    constexpr int PER_T = TK * DH / 4 / 64;  // float4 pieces per thread and tile
+    static_assert(TK * DH / 4 % 64 == 0, "whole pieces per thread");
+#pragma unroll
+    for (int it = 0; it < PER_T; ++it) {
+      const int e = (int)threadIdx.x + 64 * it;
       const int key = j * TK + (e * 4) / DH, d = (e * 4) % DH;
-      float4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-      if (key < n_eff) {
-        kv = *(const float4*)(Kg + (int64_t)key * p.k_sr + d);
-        vv = *(const float4*)(Vg + (int64_t)key * p.v_sr + d);
-      }
+      const int64_t kr = min(key, n_eff - 1);
+      float4 kv = *(const float4*)(Kg + kr * p.k_sr + d);
+      float4 vv = *(const float4*)(Vg + kr * p.v_sr + d);
+      if (key >= n_eff) kv = vv = float4{0.f, 0.f, 0.f, 0.f};
       *(float4*)&Ks[e * 4] = kv;
       *(float4*)&Vs[e * 4] = vv;
     }
