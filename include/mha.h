@@ -169,8 +169,9 @@ enum {
   MHA_KERNEL_SPLIT = 3,   /* MFMA flash kernel, waves split the keys         */
   MHA_KERNEL_DECODE = 4,  /* one query row, no matrix cores                  */
   MHA_KERNEL_WINDOW = 5,  /* MFMA flash kernel, restricted window            */
-  MHA_KERNEL_WIDE = 6     /* d_k 256, 512: waves split the head dimension; 8
-                             waves (causal d_k 512): two groups split keys   */
+  MHA_KERNEL_WIDE = 6     /* d_k 256, 512: 4 waves split the head dimension
+                             of a 32-row block; 8 waves: unmasked, two
+                             blocks; causal d_k 512, two groups split keys  */
 };
 typedef struct {
   int32_t kernel, waves, rows_per_workgroup, mask_kind;

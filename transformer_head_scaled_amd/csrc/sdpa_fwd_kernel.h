@@ -11,7 +11,7 @@
 // stream through LDS and an online softmax (running max m and sum l per
 // query row, fp32) rescales the fp32 output accumulator.
 //
-// Work decomposition.  A workgroup is 1, 2 or 4 waves of one (batch,
+// Work decomposition.  A workgroup is 1, 2, 4 or 8 waves of one (batch,
 // head); each wave owns 64 query rows as two blocks of 32 (the forms below
 // -- causal, key split, pair layout, window -- change which rows and keys a
 // wave takes).  64-key K and V tiles pass through a 2-stage LDS ring.  Scores are formed
@@ -41,9 +41,11 @@
 // to keep the weights finite: with weights p = exp2(s·c − m·c) the softmax
 // is the same for every m.  A tile is first exponentiated against the
 // current m; as long as each lane's partial row sum stays ≤ 2^8 (so every
-// weight is ≤ 2^8) the tile is accepted as is.  Otherwise -- and on the
-// first tile of a block -- the wave takes the exact path: row max, new m,
-// rescale of O and l by exp2((m_old − m_new)·c), and the weights again.
+// weight is ≤ 2^8) the tile is accepted as is.  Otherwise the wave takes
+// the exact path: row max, new m, rescale of O and l by
+// exp2((m_old − m_new)·c), and the weights again.  A block's first tile
+// with a visible key sets m to that tile's row max before its weights are
+// formed (nothing to rescale yet), so it does not take the exact path.
 // The row sums add the fp32 weights (P·V uses them rounded to the input
 // dtype; the two differ by at most 2^-9 relative per weight).
 //

@@ -8,10 +8,12 @@
 // The rules and the measurements behind them (MI355X, interleaved runs of
 // the alternatives on one box, identical results):
 //
-// * fp32: one kernel, 64 rows a workgroup.
+// * fp32: one kernel, 64 rows a workgroup (16, four lanes a row, where
+//   64-row workgroups would number fewer than the 1024 SIMDs).
 // * d = 256, 512: the wide-head kernel, 4 waves that split d per 32-row
-//   block: unmasked, two blocks a workgroup sharing the staged K/V tiles;
-//   causal, one block (at d = 512 with the key tiles split in two groups).
+//   block: unmasked, two blocks (8 waves) a workgroup sharing the staged
+//   K/V tiles; causal, one block (at d = 512 8 waves, the key tiles split
+//   between two groups of 4).
 // * A window: the flash kernel's window form, rows as in the unmasked
 //   two-block layout, at most 2 waves a workgroup while the window spans
 //   fewer than 2048 keys besides the row itself (a workgroup walks the key
