@@ -52,17 +52,11 @@ namespace {
 #ifndef GEMM_STAGES_64
 #define GEMM_STAGES_64 2
 #endif
-#ifndef GEMM_HUGE
-#define GEMM_HUGE 0
-#endif
 #ifndef GEMM_WTM_128
 #define GEMM_WTM_128 64  // per-wave tile of the 128 x 128 workgroup tile
 #endif
 #ifndef GEMM_WTN_128
 #define GEMM_WTN_128 64
-#endif
-#ifndef GEMM_STAGES_HUGE
-#define GEMM_STAGES_HUGE 2
 #endif
 #ifndef GEMM_BIG_MIN
 #define GEMM_BIG_MIN 256   // 128 x 128 tiles once there are enough to give each CU one
@@ -306,8 +300,8 @@ hipError_t launch_dt(const GemmArgs& a, hipStream_t st) {
     for (int i = 0; i < a.nprob; ++i) t += ((a.prob[i].M + tm - 1) / tm) * (int64_t)(a.N / tn);
     return t;
   };
-  if (GEMM_HUGE && a.N % 128 == 0 && tiles(256, 128) >= GEMM_BIG_MIN)
-    return launch_t<DT, 256, 128, 64, 64, GEMM_STAGES_HUGE>(a, st);  // measured slower so far: off by default
+  // (256 x 128 tiles of eight 64 x 64 waves, and 192 x 128 tiles, measured
+  // slower: three 128 x 128 workgroups a CU hide each other's waits better)
   if (a.N % 128 == 0 && tiles(128, 128) >= GEMM_BIG_MIN)
     return launch_t<DT, 128, 128, GEMM_WTM_128, GEMM_WTN_128, GEMM_STAGES_128, GEMM_BK_128>(a, st);
   // 64 x 64 tiles: 128 k a stage (64 KB of LDS, two workgroups a CU, half
