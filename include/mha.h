@@ -211,7 +211,8 @@ int mha_forward(const void* x_q, const void* x_kv, const void* Wq, const void* W
                 int64_t n_q, int64_t n_k, int64_t d_model, int32_t h, int32_t mask_kind,
                 const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes mha_forward needs for these sizes (0 for invalid sizes). */
+/* Workspace bytes mha_forward needs for these sizes (0 for invalid sizes and
+   for sizes mha_forward rejects as beyond its supported range). */
 size_t mha_forward_workspace_size(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model,
                                   int32_t h, int32_t dtype);
 
@@ -273,7 +274,8 @@ int mha_forward_add_norm(const void* x_q, const void* x_kv, const void* Wq, cons
                          int64_t d_model, int32_t h, int32_t mask_kind, const int32_t* kv_lens,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes mha_forward_add_norm needs (0 for invalid sizes). */
+/* Workspace bytes mha_forward_add_norm needs (0 for invalid sizes and for
+   sizes beyond the supported range, as mha_forward_workspace_size). */
 size_t mha_forward_add_norm_workspace_size(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model,
                                            int32_t h, int32_t dtype);
 

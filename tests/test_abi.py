@@ -148,6 +148,9 @@ def _strided(q=(512, 512, 64), k=(512, 512, 64), v=(512, 512, 64), o=(512, 512, 
     (dict(o=(0, 0, 64)), M.MHA_ERR_INVALID_ARG),           # batch stride 0 on the output
     (dict(dtype=M.MHA_F32, q=(512, 512, 66)), M.MHA_ERR_INVALID_ARG),
     (dict(k=(512, 512, 1 << 21), n_k=1024), M.MHA_ERR_UNSUPPORTED),   # K rows span > 2 GiB
+    (dict(q=(1 << 62, 512, 64)), M.MHA_ERR_INVALID_ARG),   # a stride past 2^46 bytes
+    (dict(o=(1 << 62, 512, 64)), M.MHA_ERR_INVALID_ARG),
+    (dict(q=(1 << 40, 512, 64), B=64), M.MHA_ERR_SHAPE),   # allowed strides, span past 2^46 bytes
     (dict(O=0x1000 + 512 * 2 * 2 - 16), M.MHA_ERR_ALIAS),  # O starts inside Q's span
     (dict(q=(8192, 512, 64), O=0x1000 + 8192 * 2), M.MHA_ERR_ALIAS),  # O in the gap between Q's batches
 ])
@@ -295,6 +298,12 @@ def test_workspace_size():
     assert need % 256 == 0
     assert need < 2 * (2 * B * n_q * dm + 2 * B * n_k * dm) + 4 * 256
     assert L.mha_forward_workspace_size(B, n_q, n_k, dm, 0, M.MHA_BF16) == 0
+    # sizes mha_forward rejects as beyond its range give 0 too (no overflowed
+    # byte count): a huge batch, a huge batch x rows, a huge d_model
+    for args in ((1 << 40, 64, 64, 512, 8), (65535, 1 << 20, 1 << 20, 512, 8),
+                 (4, 64, 64, 1 << 40, 8)):
+        assert L.mha_forward_workspace_size(*args, M.MHA_BF16) == 0, args
+        assert L.mha_forward_add_norm_workspace_size(*args, M.MHA_BF16) == 0, args
     assert L.mha_forward_workspace_size(B, n_q, n_k, 1000, 16, M.MHA_BF16) == 0
 
 

@@ -69,6 +69,9 @@ constexpr int64_t kMaxRows = (int64_t)1 << 30;  // rows per sequence (int32 inde
 // The MFMA kernels address one head's K/V through a buffer resource with a
 // 32-bit byte range.
 constexpr int64_t kMaxBufferBytes = ((int64_t)1 << 31) - 1;
+// No operand may span more bytes than this (far beyond any device's memory);
+// it also keeps the byte arithmetic on shapes and strides clear of overflow.
+constexpr int64_t kMaxSpanBytes = (int64_t)1 << 46;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -92,6 +95,14 @@ WsLayout ws_layout(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model, int dty
   w.z = zbytes <= w.concat ? 0 : w.total;
   w.total_an = w.z + zbytes > w.total ? w.z + zbytes : w.total;
   return w;
+}
+
+// The sizes mha_forward accepts (non-negative ones): rows per sequence for
+// int32 indexing, rows per launch for the GEMMs' int32 M, and the product
+// B·n·d_model, which ws_layout forms in 64 bits.
+bool forward_sizes_in_range(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model) {
+  return n_q <= kMaxRows && n_k <= kMaxRows && B <= 65535 && d_model <= 65536 &&
+         B * n_q <= ((int64_t)1 << 31) - 1 && B * n_k <= ((int64_t)1 << 31) - 1;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -214,10 +225,15 @@ struct Operand {
   int64_t n, d;
 };
 
-// [lo, hi) bytes an operand can touch
+// bytes from an operand's first element to one past its last (B, h, n >= 1),
+// in 128 bits so that no shape or stride the checks let through overflows
+static __int128 span_bytes(const Operand& t, int64_t B, int64_t h, size_t es) {
+  return ((__int128)t.sb * (B - 1) + (__int128)t.sh * (h - 1) + (__int128)t.sr * (t.n - 1) + t.d) *
+         (__int128)es;
+}
+// [lo, hi) bytes an operand can touch (its span checked against kMaxSpanBytes)
 static Range span_of(const Operand& t, int64_t B, int64_t h, size_t es) {
-  const int64_t last = t.sb * (B - 1) + t.sh * (h - 1) + t.sr * (t.n - 1) + t.d;
-  return range_of(t.p, (size_t)last * es);
+  return range_of(t.p, (size_t)span_bytes(t, B, h, es));
 }
 
 // Distinct (batch, head, row) of an output land on distinct elements: the
@@ -228,11 +244,11 @@ static bool rows_disjoint(const Operand& o, int64_t B, int64_t h) {
   for (int i = 0; i < 3; ++i)
     for (int j = i + 1; j < 3; ++j)
       if (dims[j].stride < dims[i].stride) std::swap(dims[i], dims[j]);
-  int64_t extent = o.d;  // elements spanned by the dimensions so far
+  __int128 extent = o.d;  // elements spanned by the dimensions so far
   for (const Dim& dm : dims) {
     if (dm.size <= 1) continue;
     if (dm.stride < extent) return false;
-    extent = dm.stride * (dm.size - 1) + extent;
+    extent = (__int128)dm.stride * (dm.size - 1) + extent;
   }
   return true;
 }
@@ -259,17 +275,26 @@ static int sdpa_impl(const char* fn, const void* Q, const void* K, const void* V
     const int64_t align = 16 / (int64_t)es;  // rows start on 16 bytes
     for (int i = 0; i < 4; ++i) {
       for (int j = 0; j < 3; ++j)
-        if (s3[i][j] < 0 || s3[i][j] % align != 0)
+        if (s3[i][j] < 0 || s3[i][j] > kMaxSpanBytes / (int64_t)es || s3[i][j] % align != 0)
           return fail(MHA_ERR_INVALID_ARG,
-                      "%s: strides must be >= 0 and multiples of %lld elements (operand %d, stride %lld)",
+                      "%s: strides must be >= 0, below 2^46 bytes and multiples of %lld elements "
+                      "(operand %d, stride %lld)",
                       fn, (long long)align, i, (long long)s3[i][j]);
       ops[i]->sb = s3[i][0], ops[i]->sh = s3[i][1], ops[i]->sr = s3[i][2];
     }
     if (!rows_disjoint(o, B, h))
       return fail(MHA_ERR_INVALID_ARG, "%s: O strides make output rows overlap", fn);
   }
+  if (B > 0 && h > 0) {
+    const bool big = (n_q > 0 && (span_bytes(q, B, h, es) > kMaxSpanBytes ||
+                                  span_bytes(o, B, h, es) > kMaxSpanBytes)) ||
+                     (n_k > 0 && (span_bytes(k, B, h, es) > kMaxSpanBytes ||
+                                  span_bytes(v, B, h, es) > kMaxSpanBytes));
+    if (big) return fail(MHA_ERR_SHAPE, "%s: an operand spans more than 2^46 bytes", fn);
+  }
   if (z.dtype != MHA_F32 && n_k > 0 &&
-      (n_k * k.sr * (int64_t)es > kMaxBufferBytes || n_k * v.sr * (int64_t)es > kMaxBufferBytes))
+      ((__int128)n_k * k.sr * (int64_t)es > kMaxBufferBytes ||
+       (__int128)n_k * v.sr * (int64_t)es > kMaxBufferBytes))
     return fail(MHA_ERR_UNSUPPORTED, "%s: one head's K/V rows span more than 2 GiB (n_k %lld)", fn,
                 (long long)n_k);
   if (B == 0 || h == 0 || n_q == 0) return ok();
@@ -384,6 +409,7 @@ int mha_sdpa_route(int32_t dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k
 size_t mha_forward_workspace_size(int64_t B, int64_t n_q, int64_t n_k, int64_t d_model,
                                   int32_t h, int32_t dtype) {
   if (B < 0 || n_q < 0 || n_k < 0 || d_model <= 0 || h <= 0 || d_model % h != 0) return 0;
+  if (!forward_sizes_in_range(B, n_q, n_k, d_model)) return 0;
   if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16) return 0;
   return ws_layout(B, n_q, n_k, d_model, dtype).total;
 }
@@ -407,8 +433,7 @@ static int forward_impl(const char* fn, const void* x_q, const void* x_kv, const
   if (d_model % h != 0)
     return fail(MHA_ERR_SHAPE, "%s: d_model %lld not divisible by h %d", fn,
                 (long long)d_model, (int)h);
-  if (n_q > kMaxRows || n_k > kMaxRows || B > 65535 || d_model > 65536 ||
-      B * n_q > ((int64_t)1 << 31) - 1 || B * n_k > ((int64_t)1 << 31) - 1)
+  if (!forward_sizes_in_range(B, n_q, n_k, d_model))
     return fail(MHA_ERR_SHAPE, "%s: size beyond the supported range", fn);
   const bool self = (x_kv == nullptr || x_kv == x_q);
   if (self && n_k != n_q)
