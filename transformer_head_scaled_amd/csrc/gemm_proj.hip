@@ -300,9 +300,9 @@ hipError_t launch_dt(const GemmArgs& a, hipStream_t st) {
     for (int i = 0; i < a.nprob; ++i) t += ((a.prob[i].M + tm - 1) / tm) * (int64_t)(a.N / tn);
     return t;
   };
-  // (256 x 128 tiles of eight 64 x 64 waves, 192 x 128 and 384 x 128 tiles
-  // measured slower: three 128 x 128 workgroups a CU hide each other's waits
-  // better)
+  // (256 x 128 tiles of eight 64 x 64 waves, 192 x 128, 384 x 128 and
+  // 64 x 128 tiles measured slower: three 128 x 128 workgroups a CU balance
+  // the bytes staged per flop against the waves that hide each other's waits)
   if (a.N % 128 == 0 && tiles(128, 128) >= GEMM_BIG_MIN)
     return launch_t<DT, 128, 128, GEMM_WTM_128, GEMM_WTN_128, GEMM_STAGES_128, GEMM_BK_128>(a, st);
   // 64 x 64 tiles: 128 k a stage (64 KB of LDS, two workgroups a CU, half
