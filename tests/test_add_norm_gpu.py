@@ -63,7 +63,8 @@ def test_add_norm_pin_through_api(pin, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("rows,d", [(1, 64), (3, 100), (1001, 512), (37, 1024), (5, 4096), (2, 4)])
+@pytest.mark.parametrize("rows,d", [(1, 64), (3, 100), (1001, 512), (37, 1024), (5, 4096), (2, 4),
+                                    (3072, 1024)])  # the benchmark's launch
 def test_add_norm_random(dtype, rows, d):
     rs = np.random.default_rng(rows * 7 + d)
     x = rounded(rs.standard_normal((rows, d)) * 2 + 0.3, dtype)[1]

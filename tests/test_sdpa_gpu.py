@@ -345,6 +345,33 @@ def test_wide_heads(dtype, d, case):
     _check(got, exp, dtype, f"{dtype} wide d={d} {case}")
 
 
+@pytest.mark.parametrize("h,d", [(2, 256), (1, 512)])
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_wide_heads_bench_launch_all_heads(h, d, mask):
+    """The wide-head launches the benchmark's head-dimension sweep times:
+    [4,2,4096,256] and [4,1,4096,512] ([N] Table 3 (A), h·d = 512), scale
+    1/sqrt(d), with the route each runs on asserted (unmasked: two 32-row
+    blocks a workgroup; causal d 512: the key split); every output of every
+    head against the oracle."""
+    B, n = 4, 4096
+    want = {"none": (8, 64), "causal": (8 if d == 512 else 4, 32)}[mask]
+    r = libmha.sdpa_route(libmha.MHA_BF16, B, h, n, n, d, mask=mask)
+    assert (r["kernel"], r["waves"], r["rows_per_workgroup"]) == ("wide",) + want, r
+    ins = synth.sdpa_inputs(5, B, h, n, n, d, dtype="bf16")
+    note(f"sdpa bf16 {mask} [{B},{h},{n},{d}] (the head-dimension sweep's launch)")
+    scale = 1 / math.sqrt(d)
+    got = _run(ins, "bf16", mask, scale=scale)
+    Q, K, V = (ins[k][1] for k in "QKV")
+    err = 0.0
+    for b in range(B):
+        for i in range(h):
+            exp, _ = oracle.attention_head(Q[b, i], K[b, i], V[b, i], scale, MASKS[mask])
+            assert np.all(np.isfinite(got[b, i])), f"head ({b},{i}): non-finite output"
+            err = max(err, float(np.max(np.abs(got[b, i] - exp))))
+    print(f"[parity] {mask} [{B},{h},{n},{d}] all heads: max-abs {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [256, 512])
 def test_wide_causal_long(dtype, d):

@@ -138,3 +138,25 @@ def test_window_routes_match_plain_and_causal():
     torch.cuda.synchronize()
     assert torch.equal(full, plain)
     assert torch.equal(causal_w, causal)
+
+
+def test_window_bench_launch_all_heads():
+    """The restricted-attention launch the benchmark times: [4,8,4096,64]
+    (the long-sequence workload's inputs), reach 256 on both sides, scale
+    1/8, with the route it runs on asserted; every output of every one of
+    the 32 heads against the oracle."""
+    B, h, n, d, reach = 4, 8, 4096, 64, 256
+    r = libmha.sdpa_route(libmha.MHA_BF16, B, h, n, n, d, window=(reach, reach))
+    assert (r["kernel"], r["waves"]) == ("window", 2), r
+    ins = synth.sdpa_inputs(5, B, h, n, n, d, dtype="bf16")
+    note(f"window bf16 [{B},{h},{n},{d}] reach {reach} (the bench's launch)")
+    got = _run(ins, "bf16", reach, reach)
+    Q, K, V = (ins[k][1] for k in "QKV")
+    err = 0.0
+    for b in range(B):
+        for i in range(h):
+            exp, _ = oracle.attention_head(Q[b, i], K[b, i], V[b, i], 0.125, window=(reach, reach))
+            assert np.all(np.isfinite(got[b, i])), f"head ({b},{i}): non-finite output"
+            err = max(err, float(np.max(np.abs(got[b, i] - exp))))
+    print(f"[parity] window reach {reach} [4,8,4096,64] all 32 heads: max-abs {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
