@@ -345,6 +345,40 @@ def test_wide_heads(dtype, d, case):
     _check(got, exp, dtype, f"{dtype} wide d={d} {case}")
 
 
+# The head-dimension sweep's other launches, [4, h, 4096, d] with h·d = 512
+# (and 1024 for h 8, d 128), and the route each runs on at that size.
+SWEEP_ROUTES = {
+    (32, 16, "none"): ("blocks", 4), (32, 16, "causal"): ("blocks", 4),
+    (16, 32, "none"): ("blocks", 4), (16, 32, "causal"): ("blocks", 4),
+    (4, 128, "none"): ("pairs", 4), (4, 128, "causal"): ("pairs", 4),
+    (8, 128, "none"): ("blocks", 4), (8, 128, "causal"): ("pairs", 4),
+}
+
+
+@pytest.mark.parametrize("key", sorted(SWEEP_ROUTES), ids=lambda k: f"h{k[0]}_d{k[1]}_{k[2]}")
+def test_head_dim_sweep_launches(key):
+    """Each launch of the benchmark's head-dimension sweep at its full size
+    and route: the first and the last head compared whole against the
+    oracle (the other heads run the same code on other rows)."""
+    h, d, mask = key
+    B, n = 4, 4096
+    r = libmha.sdpa_route(libmha.MHA_BF16, B, h, n, n, d, mask=mask)
+    assert (r["kernel"], r["waves"]) == SWEEP_ROUTES[key], r
+    ins = synth.sdpa_inputs(5, B, h, n, n, d, dtype="bf16")
+    note(f"sdpa bf16 {mask} [{B},{h},{n},{d}] (the head-dimension sweep's launch)")
+    scale = 1 / math.sqrt(d)
+    got = _run(ins, "bf16", mask, scale=scale)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    Q, K, V = (ins[k][1] for k in "QKV")
+    err = 0.0
+    for b, i in ((0, 0), (B - 1, h - 1)):
+        exp, _ = oracle.attention_head(Q[b, i], K[b, i], V[b, i], scale, MASKS[mask])
+        err = max(err, float(np.max(np.abs(got[b, i] - exp))))
+    print(f"[parity] {mask} [{B},{h},{n},{d}] heads (0,0), ({B - 1},{h - 1}): max-abs {err:.3e}",
+          flush=True)
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("h,d", [(2, 256), (1, 512)])
 @pytest.mark.parametrize("mask", ["none", "causal"])
 def test_wide_heads_bench_launch_all_heads(h, d, mask):
