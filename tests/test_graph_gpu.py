@@ -12,9 +12,10 @@ A replay that depended on state left behind by the eager call, by the
 previous replay or by the other call would show here, as would a memset node
 giving wrong results on later replays.
 
-Only calls that allocate nothing are captured: mha_forward and
-mha_forward_add_norm with their workspace given, and mha_forward_noalloc.
-With no workspace, mha_forward allocates stream-ordered memory.
+Only calls that allocate nothing are captured: every SDPA form (the strided
+one included), Add & Norm, mha_forward and mha_forward_add_norm with their
+workspace given, and mha_forward_noalloc.  With no workspace, mha_forward
+allocates stream-ordered memory.
 """
 
 import numpy as np
@@ -79,6 +80,19 @@ def test_graph_sdpa(mask):
     O = torch.empty_like(Q)
     note(f"graph sdpa bf16 {mask} [{B},{h},{n},{d}] lens 200,131")
     _replay_matches(lambda: libmha.sdpa(Q, K, V, mask=mask, seq_lens=lens, out=O), O, _other(rng))
+
+
+def test_graph_sdpa_strided():
+    """mha_sdpa_strided on [B, n, h, d] views of packed projections (the
+    layout x·W gives), O written straight into a concat-layout buffer."""
+    rng = np.random.default_rng(9107)
+    B, n, h, d = 2, 150, 3, 64
+    qkv = _dev(rng, (B, n, 3 * h * d), "bf16")
+    Q, K, V = (qkv[:, :, j * h * d:(j + 1) * h * d].view(B, n, h, d).transpose(1, 2) for j in range(3))
+    concat = torch.empty((B, n, h * d), dtype=torch.bfloat16, device="cuda")
+    O = concat.view(B, n, h, d).transpose(1, 2)
+    note(f"graph sdpa_strided bf16 causal [{B},{h},{n},{d}] packed QKV, concat out")
+    _replay_matches(lambda: libmha.sdpa_strided(Q, K, V, mask="causal", out=O), concat, _other(rng))
 
 
 def test_graph_sdpa_window():
